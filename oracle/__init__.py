@@ -1,0 +1,136 @@
+"""CPU oracle for exact attention -- TEST INFRASTRUCTURE, not the product.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the GPU library
+and never imports it.
+
+Contents
+--------
+``attention_f64`` / ``attention_rows_f64``
+    The plain definition of attention (scores, row softmax, P.V, plus the
+    natural-log logsumexp per row) in fp64, implemented in ``attention_ref.c``
+    and loaded through ctypes.  See that file's header for the passages of the
+    pages it follows.
+``tiled``
+    A numpy model of the tiled forward recurrence the pages describe (online
+    softmax, delayed normalisation, block-level causal skip).  It is used only to
+    check that the recurrence reaches the definition and to reproduce the pages'
+    printed intermediate values.
+
+Inputs are exact fp64 upcasts of the fp16/bf16 values the GPU receives, and the
+multiplier is the float32 value the GPU receives, widened to double.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attention_ref.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib_cache: dict[str, ctypes.CDLL] = {}
+
+
+def build(src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile the C oracle with gcc (no fast-math: IEEE fp64 throughout)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", "-pthread", src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (building first if absent) the oracle library at ``path``."""
+    if path in _lib_cache:
+        return _lib_cache[path]
+    if not os.path.exists(path):
+        if path != LIB_PATH:
+            raise FileNotFoundError(path)
+        build()
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lp = ctypes.POINTER(ctypes.c_int64)
+    i64 = ctypes.c_int64
+    lib.oracle_attention_f64.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                         ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.oracle_attention_f64.restype = ctypes.c_int
+    lib.oracle_attention_rows_f64.argtypes = [dp, dp, dp, lp, i64, dp, dp, i64, i64,
+                                              ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.oracle_attention_rows_f64.restype = ctypes.c_int
+    _lib_cache[path] = lib
+    return lib
+
+
+def _threads(nthreads: int | None) -> int:
+    if nthreads is not None:
+        return max(1, int(nthreads))
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def attention_f64(q, k, v, causal: bool, scale: float, nthreads: int | None = None,
+                  lib_path: str = LIB_PATH):
+    """Exact attention over [B, H, N, d] (or [N, d]) fp64 arrays.
+
+    Returns ``(o, lse)`` with ``o`` shaped like ``q`` and ``lse`` shaped like
+    ``q.shape[:-1]``.  ``scale`` is used as given (pass the float32 value the
+    GPU sees, widened to double).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"shape mismatch {q.shape} {k.shape} {v.shape}")
+    squeeze = q.ndim == 2
+    if squeeze:
+        q, k, v = q[None, None], k[None, None], v[None, None]
+    if q.ndim != 4:
+        raise ValueError("expected [B, H, N, d] or [N, d]")
+    B, H, N, d = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    lib = load(lib_path)
+    rc = lib.oracle_attention_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                  int(bool(causal)), float(scale), _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_f64 failed with code {rc}")
+    if squeeze:
+        return o[0, 0], lse[0, 0]
+    return o, lse
+
+
+def attention_rows_f64(q, k, v, rows, causal: bool, scale: float, nthreads: int | None = None,
+                       lib_path: str = LIB_PATH):
+    """Exact attention for selected query ``rows`` of one head ([N, d] inputs).
+
+    Returns ``(o_rows [R, d], lse_rows [R])``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 2 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("expected three [N, d] arrays of equal shape")
+    N, d = q.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    R = rows.shape[0]
+    o = np.empty((R, d), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    lib = load(lib_path)
+    rc = lib.oracle_attention_rows_f64(_ptr(q), _ptr(k), _ptr(v),
+                                       rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), R,
+                                       _ptr(o), _ptr(lse), N, d, int(bool(causal)), float(scale),
+                                       _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_rows_f64 failed with code {rc}")
+    return o, lse
+

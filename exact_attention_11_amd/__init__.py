@@ -1,0 +1,139 @@
+"""Fused exact-attention forward pass for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of the C ABI declared in ``include/fa2.h``; every step of
+the computation runs in the HIP kernels of ``libfa2.so``.  torch supplies device
+memory and streams only.
+
+    o, lse = exact_attention_11_amd.forward(q, k, v, causal=True)
+
+``q, k, v``: [B, H, N, d] fp16 or bf16 CUDA (HIP) tensors, contiguous.
+Returns ``o`` (same shape and dtype) and ``lse`` ([B, H, N] float32, the
+natural-log logsumexp of each row's scaled, masked scores).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa2.so")
+
+FA2_DTYPE_FP16 = 0
+FA2_DTYPE_BF16 = 1
+
+FA2_OK = 0
+FA2_ERR_NULLPTR = 1
+FA2_ERR_SHAPE = 2
+FA2_ERR_HEADDIM = 3
+FA2_ERR_DTYPE = 4
+FA2_ERR_SCALE = 5
+FA2_ERR_ALIGN = 6
+FA2_ERR_ALIAS = 7
+FA2_ERR_DEVICE = 8
+FA2_ERR_LAUNCH = 9
+
+# Every symbol include/fa2.h declares.
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_status_str", "fa2_last_hip_error")
+
+HEAD_DIMS = (64, 128, 256)
+
+
+class Fa2Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"fa2_fwd failed: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa2.so.  Raises ImportError when it has not been built.
+
+    torch is imported first so that its HIP runtime is the one the library binds
+    to (both carry the SONAME libamdhip64.so.7).
+    """
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    import torch  # noqa: F401  (binds the HIP runtime before the library loads)
+
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m exact_attention_11_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                            ctypes.c_int, vp]
+    lib.fa2_fwd.restype = ctypes.c_int
+    lib.fa2_status_str.argtypes = [ctypes.c_int]
+    lib.fa2_status_str.restype = ctypes.c_char_p
+    lib.fa2_last_hip_error.argtypes = []
+    lib.fa2_last_hip_error.restype = ctypes.c_int
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def fa2_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int,
+            causal: int, scale: float, dtype: int, stream: int) -> int:
+    """Direct call of the C entry point with raw device addresses; returns the status."""
+    return load_library().fa2_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), int(dtype),
+                                  stream)
+
+
+def fa2_status_str(status: int) -> str:
+    return load_library().fa2_status_str(int(status)).decode()
+
+
+def fa2_last_hip_error() -> int:
+    return load_library().fa2_last_hip_error()
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float16:
+        return FA2_DTYPE_FP16
+    if t.dtype == torch.bfloat16:
+        return FA2_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None):
+    """Attention forward on the GPU.  Returns ``(o, lse)``.
+
+    ``scale`` defaults to 1/sqrt(d) (computed here, not in the library).  ``out``
+    and ``lse`` may be given preallocated; ``stream`` defaults to torch's current
+    stream of the tensors' device.
+    """
+    import torch
+
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    code = _dtype_code(q)
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous [B, H, N, d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, N, d, int(bool(causal)), float(scale), code, s.cuda_stream)
+    if rc != FA2_OK:
+        raise Fa2Error(rc, fa2_status_str(rc))
+    return out, lse

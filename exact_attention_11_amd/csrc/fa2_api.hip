@@ -1,0 +1,146 @@
+// fa2_api.hip -- C ABI of the fused attention forward pass (declared in
+// include/fa2.h): argument checks, device check, instance dispatch and launch.
+//
+// Instances: element type {fp16, bf16} x head dim {64, 128, 256} x {no mask,
+// causal}.  The head-dim limit of 256 follows "FlashAttention-2: Where the Second
+// 2x Actually Comes From" (section "Limitations & open questions").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fa2.h"
+#include "fa2_fwd_kernel.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+int g_dev_arch[kMaxDevices] = {0};
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    g_last_hip_error = (int)e;
+    (void)hipGetLastError();
+    return FA2_ERR_DEVICE;
+  }
+  if (dev < kMaxDevices && g_dev_arch[dev] != 0) return g_dev_arch[dev] == 1 ? FA2_OK : FA2_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    (void)hipGetLastError();
+    return FA2_ERR_DEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                  (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+  if (dev < kMaxDevices) g_dev_arch[dev] = ok ? 1 : 2;
+  return ok ? FA2_OK : FA2_ERR_DEVICE;
+}
+
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+template <int kDType, int D, bool kCausal>
+hipError_t launch(const fa2::FwdArgs& args, hipStream_t stream) {
+  hipLaunchKernelGGL((fa2::fa2_fwd_kernel<kDType, D, kCausal>), dim3(args.n_wg), dim3(fa2::kThreads), 0, stream,
+                     args);
+  return hipGetLastError();
+}
+
+template <int kDType, int D>
+hipError_t launch_c(const fa2::FwdArgs& args, bool causal, hipStream_t stream) {
+  return causal ? launch<kDType, D, true>(args, stream) : launch<kDType, D, false>(args, stream);
+}
+
+template <int kDType>
+hipError_t launch_d(const fa2::FwdArgs& args, int64_t d, bool causal, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_c<kDType, 64>(args, causal, stream);
+    case 128: return launch_c<kDType, 128>(args, causal, stream);
+    default: return launch_c<kDType, 256>(args, causal, stream);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa2_status_str(int status) {
+  switch (status) {
+    case FA2_OK: return "ok";
+    case FA2_ERR_NULLPTR: return "null pointer for a non-empty problem";
+    case FA2_ERR_SHAPE: return "negative or too large B, H or N";
+    case FA2_ERR_HEADDIM: return "head dim must be 64, 128 or 256";
+    case FA2_ERR_DTYPE: return "dtype must be FA2_DTYPE_FP16 or FA2_DTYPE_BF16";
+    case FA2_ERR_SCALE: return "scale must be finite";
+    case FA2_ERR_ALIGN: return "pointers must be 16-byte aligned";
+    case FA2_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA2_ERR_DEVICE: return "no usable gfx950 device";
+    case FA2_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fa2_last_hip_error(void) { return g_last_hip_error; }
+
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+            int64_t d, int causal, float scale, int dtype, void* stream) {
+  g_last_hip_error = 0;
+  // ---- argument checks: no HIP call before they all pass -------------------
+  if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA2_ERR_HEADDIM;
+  if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
+  const float c2 = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+  if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) return FA2_OK;  // empty problem: nothing to do
+  // Index limits: rows fit in int32 inside the kernel, the grid in 2^31 - 1
+  // workgroups, byte sizes in 63 bits.
+  if (N > (int64_t)INT32_MAX - fa2::kBr) return FA2_ERR_SHAPE;
+  if (B > INT32_MAX || H > INT32_MAX) return FA2_ERR_SHAPE;
+  const int64_t bh = B * H;  // both < 2^31: no overflow
+  const int64_t n_qtiles = (N + fa2::kBr - 1) / fa2::kBr;
+  if (bh > (int64_t)INT32_MAX / n_qtiles) return FA2_ERR_SHAPE;
+  if (bh > (INT64_MAX / 4) / (N * d)) return FA2_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_NULLPTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA2_ERR_ALIGN;
+  const uint64_t tensor_bytes = (uint64_t)(bh * N * d) * 2;
+  const uint64_t lse_bytes = (uint64_t)(bh * N) * 4;
+  if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, tensor_bytes) ||
+      overlaps(o, tensor_bytes, v, tensor_bytes) || overlaps(lse, lse_bytes, q, tensor_bytes) ||
+      overlaps(lse, lse_bytes, k, tensor_bytes) || overlaps(lse, lse_bytes, v, tensor_bytes) ||
+      overlaps(o, tensor_bytes, lse, lse_bytes))
+    return FA2_ERR_ALIAS;
+
+  // ---- device ---------------------------------------------------------------
+  const int dev_status = check_device();
+  if (dev_status != FA2_OK) return dev_status;
+
+  fa2::FwdArgs args;
+  args.q = (const uint16_t*)q;
+  args.k = (const uint16_t*)k;
+  args.v = (const uint16_t*)v;
+  args.o = (uint16_t*)o;
+  args.lse = lse;
+  args.N = (int)N;
+  args.n_qtiles = (int)n_qtiles;
+  args.n_wg = (int)(bh * n_qtiles);
+  args.c2 = c2;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_d<0>(args, d, causal != 0, s) : launch_d<1>(args, d, causal != 0, s);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA2_ERR_LAUNCH;
+  }
+  return FA2_OK;
+}
+
+}  // extern "C"

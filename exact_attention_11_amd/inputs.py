@@ -1,0 +1,82 @@
+"""Seeded synthetic inputs and the named workloads.
+
+This module only draws random numbers and describes shapes; it holds none of
+the attention arithmetic, so both the GPU path and the CPU oracle can take their
+inputs from it.
+
+The pages measure on synthetic attention shapes (sequence lengths 512-16k,
+head dims 64 and 128, batch 8 at length 4096), and the one value distribution
+they show is i.i.d. standard normal from a fixed seed ("Flash Attention: Memory-
+Efficient Attention at Scale", section "Online softmax", the tiled example).
+The workloads below stand in for those sweeps.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str     # "fp16" or "bf16"
+    causal: bool
+    dist: str      # "normal": Q, K, V ~ N(0, 1); "peaky": Q, K ~ 3 N(0, 1), V ~ U(-1, 1)
+    what: str
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "fp16" else torch.bfloat16
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny_d64", 1, 1, 128, 64, "fp16", False, "normal",
+                 "single head, 128 tokens, head dim 64, no mask"),
+        Workload("b8h16_n2048_d64", 8, 16, 2048, 64, "fp16", False, "normal",
+                 "batch 8 x 16 heads, 2048 tokens, head dim 64, no mask (16k tokens)"),
+        Workload("b8h16_n2048_d128_causal", 8, 16, 2048, 128, "bf16", True, "normal",
+                 "batch 8 x 16 heads, 2048 tokens, head dim 128, causal"),
+        Workload("b1h32_n16384_d128_causal", 1, 32, 16384, 128, "fp16", True, "normal",
+                 "batch 1 x 32 heads, 16384 tokens, head dim 128, causal (long context)"),
+        Workload("b4h8_n4099_d256_peaky", 4, 8, 4099, 256, "bf16", False, "peaky",
+                 "batch 4 x 8 heads, 4099 tokens (ragged), head dim 256, peaky scores, no mask"),
+    ]
+}
+
+
+def make_qkv(B: int, H: int, N: int, d: int, dtype, dist: str = "normal", seed: int = 0):
+    """Host tensors q, k, v of shape [B, H, N, d] in ``dtype`` (fp16/bf16).
+
+    Drawn in fp32 from ``torch.Generator('cpu').manual_seed(seed)`` in the order
+    Q, K, V, then rounded once to ``dtype`` (round to nearest even).
+    """
+    if isinstance(dtype, str):
+        dtype = torch.float16 if dtype == "fp16" else torch.bfloat16
+    g = torch.Generator("cpu").manual_seed(seed)
+    shape = (B, H, N, d)
+    if dist == "normal":
+        q = torch.randn(shape, generator=g, dtype=torch.float32)
+        k = torch.randn(shape, generator=g, dtype=torch.float32)
+        v = torch.randn(shape, generator=g, dtype=torch.float32)
+    elif dist == "peaky":
+        q = torch.randn(shape, generator=g, dtype=torch.float32) * 3.0
+        k = torch.randn(shape, generator=g, dtype=torch.float32) * 3.0
+        v = torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0
+    else:
+        raise ValueError(dist)
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+def workload_inputs(w: Workload, seed: int = 0):
+    return make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, w.dist, seed)

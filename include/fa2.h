@@ -1,0 +1,100 @@
+/*
+ * fa2.h -- C ABI of the fused exact-attention forward pass for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation.  For every batch b < B, head h < H and query row r < N:
+ *
+ *   s_rc  = scale * sum_t Q[b,h,r,t] * K[b,h,c,t]       for allowed keys c
+ *   O[b,h,r,:] = sum_c softmax_c(s_r.) * V[b,h,c,:]
+ *   lse[b,h,r] = log(sum_c exp(s_rc))                   (natural log)
+ *
+ * where the allowed keys are c < N, and with a causal mask only c <= r.
+ *  - Standard attention (scores, row softmax, P.V): "Flash Attention:
+ *    Memory-Efficient Attention at Scale" (Lesson 6.6), section "A quick recap
+ *    of standard attention"; "Flash Attention 2", section "Standard Attention".
+ *  - The causal mask (0 for key <= query, -inf otherwise, so masked keys carry
+ *    no weight): "6.2 FlashAttention V2 in depth", section 5.1, and "Flash
+ *    Attention 2", section "Causal masking".
+ *  - The per-row statistic L = m + log(l), i.e. the logsumexp of the scaled,
+ *    masked scores, returned next to O: "6.2 FlashAttention V2 in depth",
+ *    sections 6.1 and 7.1.
+ *  - The result is exact attention, computed tile by tile without ever storing
+ *    the N x N score matrix: "6.2 FlashAttention V2 in depth", sections 2-6.
+ *
+ * Everything here is plain C: pointers, sizes and an opaque stream handle.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O. */
+typedef enum {
+  FA2_DTYPE_FP16 = 0, /* IEEE binary16 */
+  FA2_DTYPE_BF16 = 1  /* bfloat16 */
+} fa2_dtype;
+
+/* Return codes.  Every failure is reported before anything is launched, except
+ * FA2_ERR_LAUNCH. */
+typedef enum {
+  FA2_OK = 0,
+  FA2_ERR_NULLPTR = 1, /* a pointer argument is NULL while the problem is not empty */
+  FA2_ERR_SHAPE = 2,   /* B, H or N is negative, or the problem is too large to index */
+  FA2_ERR_HEADDIM = 3, /* d is not 64, 128 or 256 */
+  FA2_ERR_DTYPE = 4,   /* dtype is not a fa2_dtype value */
+  FA2_ERR_SCALE = 5,   /* scale is NaN, infinite, or so large that scale*log2(e) overflows */
+  FA2_ERR_ALIGN = 6,   /* a pointer is not 16-byte aligned */
+  FA2_ERR_ALIAS = 7,   /* o or lse overlaps an input, or o overlaps lse */
+  FA2_ERR_DEVICE = 8,  /* no current HIP device, or it is not a gfx950 */
+  FA2_ERR_LAUNCH = 9   /* the HIP launch itself reported an error */
+} fa2_status;
+
+/*
+ * fa2_fwd -- enqueue the forward pass on `stream` and return without waiting.
+ *
+ * q, k, v : device pointers to [B, H, N, d] arrays of `dtype`, contiguous and
+ *           row-major (d innermost; strides d, N*d, H*N*d elements).  Read only.
+ * o       : device pointer to a [B, H, N, d] array of `dtype`; written.
+ * lse     : device pointer to a [B, H, N] float32 array; written with the
+ *           natural-log logsumexp of each row's scaled, masked scores.
+ * B, H, N : batch, heads, sequence length.  Any N >= 1 (no multiple of a tile
+ *           is required).  If B*H*N == 0 the call does nothing and returns
+ *           FA2_OK; pointers are then not inspected.
+ * d       : head dimension, 64, 128 or 256.
+ * causal  : nonzero applies the causal mask (key index <= query index).
+ * scale   : multiplier of the scores; any finite value, including 0 and
+ *           negative values.  The library never substitutes 1/sqrt(d).
+ * dtype   : a fa2_dtype value.
+ * stream  : a hipStream_t of the current device (NULL = the null stream).
+ *
+ * Ownership: the caller allocates and owns every buffer.  The library keeps no
+ * state between calls beyond a per-device cache of the device check, allocates
+ * no memory and needs no workspace.  All pointers must be 16-byte aligned and
+ * reside on the current device; o and lse must not overlap each other or q, k, v.
+ *
+ * Errors: argument checks run before any HIP call; on a failed check nothing is
+ * written or launched.  FA2_ERR_DEVICE is returned when the current device
+ * cannot be queried or is not gfx950.  FA2_ERR_LAUNCH carries a launch error;
+ * faults during execution surface at the caller's next synchronisation, as for
+ * any HIP kernel.  No C++ exception crosses this boundary.
+ */
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int64_t B, int64_t H, int64_t N, int64_t d,
+            int causal, float scale, int dtype, void* stream);
+
+/* Static, NUL-terminated description of a return code (never NULL). */
+const char* fa2_status_str(int status);
+
+/* Last HIP error code seen by a failing fa2_fwd call on this thread (0 if none);
+ * useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
+int fa2_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

@@ -1,0 +1,116 @@
+"""The C ABI library: it loads, exports every symbol include/fa2.h declares, and
+its argument checks return their codes without touching a device (CPU only)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_11_amd as fa
+from exact_attention_11_amd import build as hip_build
+
+HEADER = os.path.join(hip_build.INCLUDE, "fa2.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        hip_build.build()
+    return fa.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa2_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared_functions() == sorted(fa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for code in range(0, 10):
+        s = fa.fa2_status_str(code)
+        assert s and s != "unknown status"
+    assert fa.fa2_status_str(123) == "unknown status"
+    assert fa.fa2_status_str(-1) == "unknown status"
+
+
+# Fake but aligned, distinct, non-overlapping addresses: every call below must be
+# rejected by the host-side checks before any HIP call is made.
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def _call(B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=0, q=Q, k=K, v=V, o=O, lse=L):
+    return fa.fa2_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(B=-1), fa.FA2_ERR_SHAPE), (dict(H=-2), fa.FA2_ERR_SHAPE), (dict(N=-1), fa.FA2_ERR_SHAPE),
+    (dict(N=2 ** 31), fa.FA2_ERR_SHAPE), (dict(B=2 ** 20, H=2 ** 20, N=1024), fa.FA2_ERR_SHAPE),
+    (dict(d=32), fa.FA2_ERR_HEADDIM), (dict(d=96), fa.FA2_ERR_HEADDIM), (dict(d=512), fa.FA2_ERR_HEADDIM),
+    (dict(dtype=2), fa.FA2_ERR_DTYPE), (dict(dtype=-1), fa.FA2_ERR_DTYPE),
+    (dict(scale=math.nan), fa.FA2_ERR_SCALE), (dict(scale=math.inf), fa.FA2_ERR_SCALE),
+    (dict(scale=-math.inf), fa.FA2_ERR_SCALE), (dict(scale=3.0e38), fa.FA2_ERR_SCALE),
+    (dict(q=0), fa.FA2_ERR_NULLPTR), (dict(k=0), fa.FA2_ERR_NULLPTR), (dict(v=0), fa.FA2_ERR_NULLPTR),
+    (dict(o=0), fa.FA2_ERR_NULLPTR), (dict(lse=0), fa.FA2_ERR_NULLPTR),
+    (dict(q=Q + 8), fa.FA2_ERR_ALIGN), (dict(o=O + 2), fa.FA2_ERR_ALIGN), (dict(lse=L + 4), fa.FA2_ERR_ALIGN),
+    (dict(o=Q), fa.FA2_ERR_ALIAS), (dict(o=K + 1024), fa.FA2_ERR_ALIAS), (dict(lse=V + 16), fa.FA2_ERR_ALIAS),
+    (dict(lse=O + 512), fa.FA2_ERR_ALIAS),
+])
+def test_argument_checks(lib, kwargs, code):
+    assert _call(**kwargs) == code
+
+
+@pytest.mark.parametrize("kwargs", [dict(B=0), dict(H=0), dict(N=0), dict(B=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_empty_problem_is_a_no_op(lib, kwargs):
+    assert _call(**kwargs) == fa.FA2_OK
+
+
+def test_inputs_may_alias_each_other_when_no_device(lib):
+    # q, k, v may share memory (they are only read); with no GPU the call gets
+    # past every argument check and stops at the device check.
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    assert _call(q=Q, k=Q, v=Q) == fa.FA2_ERR_DEVICE
+
+
+def test_valid_call_without_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    for d in (64, 128, 256):
+        for dtype in (0, 1):
+            assert _call(d=d, dtype=dtype, causal=1, N=4099) == fa.FA2_ERR_DEVICE
+    assert fa.fa2_last_hip_error() != 0
+
+
+def test_single_hip_runtime_in_process(lib):
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+
+
+def test_python_forward_rejects_bad_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)  # host tensors
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q[:, :, :4])
+    with pytest.raises(TypeError):
+        fa.forward(q.float(), q.float(), q.float())

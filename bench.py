@@ -1,0 +1,226 @@
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the forward pass over the whole workload (inputs already
+resident in HBM).  The default workload is the long-context causal one
+(B=1, H=32, N=16384, d=128, fp16), the largest head-dim-128 configuration.
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+Metric: forward TFLOP/s with FLOP = 4*B*H*N^2*d, halved under a causal mask.
+``roofline`` relates the kernel's average launch time (HIP events on the launch
+stream) to the dense fp16/bf16 MFMA peak of MI355X (2.5 PFLOP/s).
+``cpu_baseline`` times the fp64 CPU oracle on a bounded, strided sample of the
+same workload's query rows on all host cores and scales it to TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+DEFAULT_WORKLOAD = "b1h32_n16384_d128_causal"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
+                  for f in ("fa2_fwd_kernel.h", "fa2_api.hip")]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def flop_count(B: int, H: int, N: int, d: int, causal: bool) -> float:
+    f = 4.0 * B * H * N * N * d
+    return f / 2.0 if causal else f
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"fa2_fwd_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_digest:\s*(\w+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_val or m_src.group(1) != kernel_source_digest():
+        return None
+    return float(m_val.group(1))
+
+
+def host_threads() -> int:
+    """Threads for the CPU oracle: the process's CPU share (OMP_NUM_THREADS when
+    set, else the affinity mask)."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, q, k, v, target_s: float = 12.0):
+    """Time the fp64 oracle on a strided sample of the workload's query rows.
+
+    Rows are strided over the whole sequence, so the mix of causal row lengths
+    matches the full workload; heads are taken in order.  A 64-row run sizes the
+    sample to about ``target_s`` seconds of wall time.
+    """
+    import numpy as np
+
+    import oracle
+
+    threads = host_threads()
+    scale = float(np.float32(w.scale))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def run(rows_per_head: int, n_heads: int):
+        flop, secs = 0.0, 0.0
+        stride = max(1, w.N // rows_per_head)
+        for i in range(n_heads):
+            b, h = heads[i]
+            qq, kk, vv = (t[b, h].double().numpy() for t in (q, k, v))
+            rows = np.arange(i % stride, w.N, stride, dtype=np.int64)[:rows_per_head]
+            t0 = time.perf_counter()
+            oracle.attention_rows_f64(qq, kk, vv, rows, w.causal, scale, nthreads=threads)
+            secs += time.perf_counter() - t0
+            keys = float((rows + 1).sum()) if w.causal else float(len(rows)) * w.N
+            flop += 4.0 * w.d * keys
+        return flop, secs
+
+    _, t_cal = run(64, 1)
+    total_rows = max(64, int(64 * target_s / max(t_cal, 1e-3)))
+    rows_per_head = min(w.N, total_rows)
+    n_heads = max(1, min(len(heads), total_rows // rows_per_head))
+    flop, secs = run(rows_per_head, n_heads)
+    return {
+        "value": flop / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n_heads} head(s) x {rows_per_head} strided query rows of {w.name}: "
+                  f"{flop / 1e9:.1f} GFLOP in {secs:.1f} s (fp64 three-stage oracle)",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the attention forward pass here runs on a single MI355X, "
+              "so --gpus must be 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 2, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 5 times")
+        return 0
+
+    import exact_attention_11_amd as fa
+    from exact_attention_11_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    log(f"workload {w.name}: {w.what}")
+    q, k, v = workload_inputs(w, seed=0)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.forward(dq, dk, dv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    flop = flop_count(w.B, w.H, w.N, w.d, w.causal)
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (avg_launch_ms * 1e-3) / 1e12
+    log(f"{args.steps} steps: {ms_per_step:.4f} ms/step (events), launch avg {avg_launch_ms:.4f} ms, "
+        f"min {min(launch_ms):.4f} ms, wall {wall_s * 1e3 / args.steps:.4f} ms/step -> {value:.1f} TFLOP/s")
+
+    traffic = recorded_traffic(w.name)
+    result = {
+        "metric": "attention fwd TFLOP/s and % of MI355X FP16/BF16 MFMA peak, hd128 seq 2k-16k",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "inputs": w.dist, "flop_per_step": flop, "kernel_source_digest": kernel_source_digest()},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of the workload ...")
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

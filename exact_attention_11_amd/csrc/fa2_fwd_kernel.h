@@ -174,7 +174,7 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src_head,
 }
 
 template <int kDType, int D, bool kCausal>
-__global__ __launch_bounds__(kThreads) void fa2_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_kernel(FwdArgs a) {
   typedef Elem<kDType> E;
   typedef typename E::V8 V8;
   constexpr int CPR = D / 8;

@@ -66,8 +66,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 
 
 def _threads(nthreads: int | None) -> int:
+    """Explicit count, else OMP_NUM_THREADS when set, else the affinity mask."""
     if nthreads is not None:
         return max(1, int(nthreads))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
     try:
         return max(1, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover

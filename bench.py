@@ -32,7 +32,7 @@ PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
 DEFAULT_WORKLOAD = "b1h32_n16384_d128_causal"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
-                  for f in ("fa2_fwd_kernel.h", "fa2_api.hip")]
+                  for f in ("fa2_common.h", "fa2_fwd_4wave.h", "fa2_fwd_8wave.h", "fa2_api.hip")]
 
 
 def log(msg: str) -> None:

@@ -11,7 +11,8 @@
 #include <cstring>
 
 #include "fa2.h"
-#include "fa2_fwd_kernel.h"
+#include "fa2_fwd_4wave.h"
+#include "fa2_fwd_8wave.h"
 
 namespace {
 
@@ -48,10 +49,18 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Query rows per workgroup of the kernel that serves head dim d.
+int64_t rows_per_workgroup(int64_t d) { return d == 256 ? fa2::w4::kBr : fa2::w8::kBr; }
+
 template <int kDType, int D, bool kCausal>
 hipError_t launch(const fa2::FwdArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL((fa2::fa2_fwd_kernel<kDType, D, kCausal>), dim3(args.n_wg), dim3(fa2::kThreads), 0, stream,
-                     args);
+  if constexpr (D == 256) {
+    hipLaunchKernelGGL((fa2::w4::fa2_fwd_4wave<kDType, D, kCausal>), dim3(args.n_wg), dim3(fa2::w4::kThreads), 0,
+                       stream, args);
+  } else {
+    hipLaunchKernelGGL((fa2::w8::fa2_fwd_8wave<kDType, D, kCausal>), dim3(args.n_wg), dim3(fa2::w8::kThreads), 0,
+                       stream, args);
+  }
   return hipGetLastError();
 }
 
@@ -103,10 +112,11 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   if (B == 0 || H == 0 || N == 0) return FA2_OK;  // empty problem: nothing to do
   // Index limits: rows fit in int32 inside the kernel, the grid in 2^31 - 1
   // workgroups, byte sizes in 63 bits.
-  if (N > (int64_t)INT32_MAX - fa2::kBr) return FA2_ERR_SHAPE;
+  if (N > (int64_t)INT32_MAX - 256) return FA2_ERR_SHAPE;
   if (B > INT32_MAX || H > INT32_MAX) return FA2_ERR_SHAPE;
   const int64_t bh = B * H;  // both < 2^31: no overflow
-  const int64_t n_qtiles = (N + fa2::kBr - 1) / fa2::kBr;
+  const int64_t br = rows_per_workgroup(d);
+  const int64_t n_qtiles = (N + br - 1) / br;
   if (bh > (int64_t)INT32_MAX / n_qtiles) return FA2_ERR_SHAPE;
   if (bh > (INT64_MAX / 4) / (N * d)) return FA2_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULLPTR;

@@ -1,0 +1,126 @@
+// fa2_common.h -- pieces shared by the gfx950 attention forward kernels:
+// vector types, the per-element-type MFMA and conversions, LDS copy and
+// barrier primitives, cross-half reductions and the kernel argument block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa2 {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA2_LDS __attribute__((address_space(3)))
+
+// Lazy-rescale threshold in log2 units: the reference max of a row only moves
+// when a tile's row max exceeds it by more than this, so unnormalised weights
+// stay below 2^kTau (far inside the fp16 range).
+constexpr float kTau = 8.0f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int N;         // sequence length
+  int n_qtiles;  // ceil(N / query rows per workgroup)
+  int n_wg;      // B * H * n_qtiles
+  float c2;      // scale * log2(e)
+};
+
+// Element-type specific pieces: the MFMA and the fp32 -> storage conversion.
+template <int kDType> struct Elem;
+template <> struct Elem<0> {  // fp16
+  typedef f16x8 V8;
+  __device__ static inline f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float a, float b) {  // round to nearest even
+    f16x2 h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+};
+template <> struct Elem<1> {  // bf16
+  typedef bf16x8 V8;
+  __device__ static inline f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float a, float b) {  // round to nearest even
+    bf16x2 h = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+};
+
+// One global_load_lds_dwordx4: every lane copies 16 bytes from its own global
+// address to lds_base + 16 * lane (lds_base is wave-uniform and goes in M0).
+// Written as inline asm so that the compiler does not track it: the compiler
+// would otherwise wait for every outstanding LDS copy before any LDS read,
+// while the kernels wait with exact counts (s_waitcnt vmcnt) for the tile they
+// need.
+__device__ __forceinline__ void dma16(const void* g, FA2_LDS void* lds_base) {
+  const uint32_t m0v = (uint32_t)(size_t)lds_base;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
+}
+// The same copy addressed as a wave-uniform base (SGPR pair) plus a per-lane
+// 32-bit byte offset.
+__device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, FA2_LDS void* lds_base) {
+  const uint32_t m0v = (uint32_t)(size_t)lds_base;
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0v) : "memory");
+}
+
+// s_waitcnt vmcnt(n) followed by a workgroup barrier.  The explicit count lets
+// later copies stay in flight across the barrier.
+template <int N> __device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+// Same, and also every LDS access of this wave has completed first.
+template <int N> __device__ __forceinline__ void wait_vm_lds_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+// All of this wave's LDS accesses have completed, then a workgroup barrier:
+// after it the buffers this wave read may be overwritten and what it wrote is
+// visible.
+__device__ __forceinline__ void lds_done_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second.  With x in both, one result holds this lane's own
+// value and the other the value of lane l ^ 32 (which one depends on the half),
+// so a symmetric combination of the two is the combination across the pair.
+__device__ __forceinline__ u32x2 pair32(float x) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                                     false));
+}
+__device__ __forceinline__ float max_pair32(float x) {
+  const u32x2 r = pair32(x);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_pair32(float x) {
+  const u32x2 r = pair32(x);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup id -> (head, query tile).  Consecutive dispatch ids go round-robin
+// over the 8 XCDs; regroup them so that each XCD walks a contiguous range of
+// heads (its L2 then serves that head's K/V to every query tile).  Under a
+// causal mask the query tiles of a head are issued heaviest (last) first.
+__device__ __forceinline__ void wg_to_tile(const FwdArgs& a, bool causal, int& bh, int& qtile) {
+  const int w = blockIdx.x;
+  int sidx = w;
+  if ((a.n_wg & 7) == 0) sidx = (w & 7) * (a.n_wg >> 3) + (w >> 3);
+  bh = sidx / a.n_qtiles;
+  const int it = sidx - bh * a.n_qtiles;
+  qtile = causal ? (a.n_qtiles - 1 - it) : it;
+}
+
+}  // namespace fa2

@@ -1,94 +1,37 @@
-// fa2_fwd_kernel.h -- fused exact-attention forward pass for gfx950 (CDNA4).
+// fa2_fwd_4wave.h -- fused exact-attention forward pass for gfx950, four
+// wavefronts per workgroup.  Used for head dim 256, whose unnormalised output
+// (128 fp32 registers per lane) leaves room for one wavefront per SIMD only.
 //
-// One workgroup owns one tile of kBr = 128 query rows of one (batch, head) and
-// streams the key/value tiles of that head through LDS, kBc = 64 keys at a time.
-// The N x N score matrix never leaves registers.  What the pages fix, and what
-// this kernel does with it:
-//
-//  * Query tiles outside, key/value tiles inside; each query tile is loaded once
-//    and its output written once ("6.2 FlashAttention V2 in depth", section 2.2).
-//    The grid runs over (query tile x head x batch), so one long sequence at
-//    batch 1 still fills the chip ("FlashAttention-2: Where the Second 2x
-//    Actually Comes From", section "Parallelism over sequence length").
-//  * Split-Q: each of the 4 wavefronts owns 32 whole query rows and sees the
-//    full key tile, so row max and row sum never cross wavefronts
-//    ("6.2 FlashAttention V2 in depth", section 4.2).
-//  * Online softmax with an unnormalised output accumulator, divided by the row
-//    sum once after the key loop, and the logsumexp L = m + log l kept per row
-//    ("6.2 FlashAttention V2 in depth", sections 3.2, 6.1 and 7.1).
-//  * Causal block classes: key tiles past the query tile are never visited,
-//    tiles crossing the diagonal are masked element by element, the rest run
-//    unmasked ("6.2 FlashAttention V2 in depth", section 5.3).
-//
-// gfx950 mapping (prior art adapted, not copied):
-//  * Both products run on v_mfma_f32_32x32x16_{f16,bf16} with fp32 accumulation.
-//    Scores are formed transposed, S^T = K Q^T, so each lane holds 16 keys of a
-//    single query per 32x32 block: a row max or row sum is an in-lane reduction
-//    plus one v_permlane32_swap exchange with the partner lane (l ^ 32).
-//  * The output is accumulated transposed too, O^T += V^T P^T: the probabilities
-//    leave the score accumulator already in the B-operand layout (the key order
-//    inside an MFMA k-step is permuted consistently on both operands), and V^T
-//    fragments come straight from the row-major V tile in LDS through
-//    ds_read_b64_tr_b16.
-//  * K and V tiles go global -> LDS with global_load_lds_dwordx4 (no register
-//    staging), into two single buffers that alternate: the next K tile streams
-//    in under the softmax and P.V of the current tile, the next V tile under the
-//    next S = K Q^T.  16-byte chunks are XOR-swizzled per row so that the
-//    fragment reads of one instruction fall in distinct LDS banks.
-//  * exp2 with the multiplier and log2(e) folded into one FMA.  The running max
-//    used as the exponent's reference is only moved when a row's tile max
-//    exceeds it by more than kTau (log2 units), so the O rescale runs rarely;
-//    the weights then stay below 2^kTau, and the result is the same
-//    mathematically (the final division and L use the same reference).
-//  * Workgroup ids are remapped so that the round-robin dispatch over the 8 XCDs
-//    gives each XCD a contiguous range of heads (its L2 keeps that head's K/V),
-//    and causal query tiles are issued heaviest first.
+// One workgroup owns kBr = 128 query rows of one (batch, head) and streams the
+// key/value tiles of that head through LDS, kBc = 64 keys at a time; the N x N
+// score matrix never leaves registers.  From the pages:
+//  * query tiles outside, key/value tiles inside; Q loaded once, O written once
+//    ("6.2 FlashAttention V2 in depth", section 2.2); the grid runs over
+//    (query tile x head x batch) ("FlashAttention-2: Where the Second 2x
+//    Actually Comes From", section "Parallelism over sequence length");
+//  * split-Q: each wavefront owns 32 whole query rows ("6.2 FlashAttention V2
+//    in depth", section 4.2);
+//  * online softmax with an unnormalised accumulator divided once at the end,
+//    and L = m + log l per row (same page, sections 3.2, 6.1, 7.1);
+//  * causal block classes: skip, mask on the diagonal, plain below it (same
+//    page, section 5.3).
+// gfx950 mapping: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16, so each
+// lane holds 16 keys of one query per 32x32 block (row max and sum are in-lane
+// plus one v_permlane32_swap); V^T fragments come from the row-major V tile via
+// ds_read_b64_tr_b16; K and V tiles alternate in two single LDS buffers filled
+// by global_load_lds (the next K tile streams under softmax and P.V, the next V
+// tile under the next S); chunks are XOR-swizzled for conflict-free reads.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "fa2_common.h"
 
 namespace fa2 {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-#define FA2_LDS __attribute__((address_space(3)))
+namespace w4 {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per K/V tile
-constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
-
-// Element-type specific pieces: the MFMA and the fp32 -> storage conversion.
-template <int kDType> struct Elem;
-template <> struct Elem<0> {  // fp16
-  typedef f16x8 V8;
-  __device__ static inline f32x16 mfma(V8 a, V8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  __device__ static inline uint32_t pack2(float a, float b) {  // round to nearest even
-    f16x2 h = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, h);
-  }
-};
-template <> struct Elem<1> {  // bf16
-  typedef bf16x8 V8;
-  __device__ static inline f32x16 mfma(V8 a, V8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  __device__ static inline uint32_t pack2(float a, float b) {  // round to nearest even
-    bf16x2 h = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, h);
-  }
-};
 
 // XOR swizzles of the 16-byte chunk index inside a tile row.
 //  K: the A-operand read of one MFMA touches 32 rows at the same logical chunk;
@@ -101,55 +44,6 @@ template <int D> __device__ __forceinline__ int swz_k(int row) {
 }
 template <int D> __device__ __forceinline__ int swz_v(int row) {
   return D == 64 ? (((row >> 1) & 1) << 2) : ((row & 3) << 2);
-}
-
-// s_waitcnt vmcnt(n) followed by a workgroup barrier.  The explicit count lets
-// the other buffer's load stay in flight across the barrier.
-template <int N> __device__ __forceinline__ void wait_vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(N) : "memory");
-}
-// All of this wave's LDS reads have returned, then a workgroup barrier: after it
-// the buffer may be overwritten.
-__device__ __forceinline__ void lds_done_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// v_permlane32_swap exchanges the upper half of its first operand with the
-// lower half of its second.  With x in both, one result holds this lane's own
-// value and the other the value of lane l ^ 32 (which one depends on the half),
-// so a symmetric combination of the two is the combination across the pair.
-__device__ __forceinline__ u32x2 pair32(float x) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false));
-}
-__device__ __forceinline__ float max_pair32(float x) {
-  const u32x2 r = pair32(x);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_pair32(float x) {
-  const u32x2 r = pair32(x);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-struct FwdArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* o;
-  float* lse;
-  int N;         // sequence length
-  int n_qtiles;  // ceil(N / kBr)
-  int n_wg;      // B * H * n_qtiles
-  float c2;      // scale * log2(e)
-};
-
-// One global_load_lds_dwordx4: every lane copies 16 bytes from its own global
-// address to lds_base + 16 * lane (lds_base is wave-uniform and goes in M0).
-// Written as inline asm so that the compiler does not track it: the compiler
-// would otherwise wait for every outstanding LDS copy before any LDS read, while
-// the loop below waits with exact counts (s_waitcnt vmcnt) for the tile it needs.
-__device__ __forceinline__ void dma16(const void* g, FA2_LDS void* lds_base) {
-  const uint32_t m0v = (uint32_t)(size_t)lds_base;
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
 }
 
 // Issue the global -> LDS copy of one kBc x D tile (rows kv0.., clamped to N-1).
@@ -174,14 +68,13 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src_head,
 }
 
 template <int kDType, int D, bool kCausal>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdArgs a) {
   typedef Elem<kDType> E;
   typedef typename E::V8 V8;
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;  // MFMA k-steps of S = K Q^T
   constexpr int DB = D / 32;  // 32-wide blocks of the output columns
   constexpr int kLoads = kBc * CPR / (64 * kWaves);
-  constexpr float kLn2 = 0.69314718055994530942f;
   constexpr float kNegInf = -__builtin_huge_valf();
 
   __shared__ __attribute__((aligned(1024))) uint16_t sK_[kBc * D];
@@ -190,14 +83,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_kernel(Fwd
   FA2_LDS uint16_t* const sV = (FA2_LDS uint16_t*)sV_;
 
   const int N = a.N;
-  // Workgroup -> (head, query tile).  Consecutive dispatch ids go round-robin
-  // over the 8 XCDs; regroup so each XCD walks a contiguous range of heads.
-  const int w = blockIdx.x;
-  int sidx = w;
-  if ((a.n_wg & 7) == 0) sidx = (w & 7) * (a.n_wg >> 3) + (w >> 3);
-  const int bh = sidx / a.n_qtiles;
-  const int it = sidx - bh * a.n_qtiles;
-  const int qtile = kCausal ? (a.n_qtiles - 1 - it) : it;  // causal: heaviest first
+  int bh, qtile;
+  wg_to_tile(a, kCausal, bh, qtile);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -366,4 +253,5 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_kernel(Fwd
   }
 }
 
+}  // namespace w4
 }  // namespace fa2

@@ -1,0 +1,399 @@
+// fa2_fwd_8wave.h -- fused exact-attention forward pass for gfx950 with eight
+// wavefronts per workgroup in two alternating groups (head dims 64 and 128).
+//
+// What the pages fix, and where it lives here:
+//  * Query tiles outside, key/value tiles inside; Q is loaded once and O written
+//    once per query tile ("6.2 FlashAttention V2 in depth", section 2.2).  The
+//    grid covers (query tile x head x batch), so one long sequence at batch 1
+//    still fills the chip ("FlashAttention-2: Where the Second 2x Actually Comes
+//    From", section "Parallelism over sequence length").
+//  * Split-Q: each wavefront owns 32 whole query rows and sees every key of the
+//    tile, so row max and row sum never cross wavefronts ("6.2 FlashAttention V2
+//    in depth", section 4.2).
+//  * Online softmax with an unnormalised output, divided by the row sum once
+//    after the key loop, and the per-row statistic L = m + log l (same page,
+//    sections 3.2, 6.1 and 7.1).
+//  * Causal block classes: tiles past the query tile are never visited, tiles
+//    crossing the diagonal are masked element by element (same page, 5.3).
+//
+// gfx950 design (the pages' A100 kernel is prior art, not the blueprint):
+//  * Work split.  A workgroup owns 256 query rows.  Waves 0-3 (group 0) and
+//    4-7 (group 1) put one wave of each group on every SIMD.  Each step of the
+//    key loop has two phases separated by workgroup barriers; in every phase
+//    one group runs its matrix products (P.V of the previous tile, then
+//    S = K Q^T of the current one) while the other runs the softmax of its
+//    scores, so MFMA and VALU work of the two waves on a SIMD overlap.  The
+//    same overlap idea is what the pages credit to the Hopper redesign
+//    ("Flash Attention: Memory-Efficient Attention at Scale", section "Flash
+//    Attention 3"); here it comes from wave scheduling alone.
+//  * Products.  Both run on v_mfma_f32_32x32x16 with fp32 accumulation, scores
+//    transposed (S^T = K Q^T): a lane holds 16 keys of one query per 32x32 block,
+//    so row max and row sum are in-lane plus one v_permlane32_swap.  O^T += V^T P^T
+//    takes the probabilities straight from the score registers as its B operand:
+//    the rows of each K tile are stored in LDS with bits 2 and 3 of the row index
+//    swapped, which makes the 8 keys a lane holds for one MFMA k-step consecutive.
+//  * Data movement.  K and V tiles go global -> LDS with global_load_lds (no
+//    register staging), two tiles ahead, into three K and three V slots.  Each V
+//    tile is transposed once per workgroup (ds_read_b64_tr_b16 + ds_write_b64,
+//    half by each group in its softmax phase) into one of two V^T slots, so the
+//    P.V operand reads are full-rate ds_read_b128.  16-byte chunks are
+//    XOR-swizzled per row so that every read and write instruction is free of
+//    bank conflicts.
+//  * Softmax.  exp2 with the multiplier and log2(e) folded into one FMA; the
+//    row sum adds the fp32 weights with plain adds (v_dot2 would be cheaper in
+//    instructions, but it stalls behind the other wave's MFMAs on the same
+//    SIMD); the reference max of a row moves only
+//    when a tile's row max exceeds it by more than kTau, so the O rescale is
+//    rare; the result is the same mathematically.
+//  * Scheduling.  Workgroups are remapped so each XCD walks a contiguous range
+//    of heads (L2 reuse of K/V); causal query tiles go heaviest first.
+#pragma once
+
+#include "fa2_common.h"
+
+namespace fa2 {
+namespace w8 {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBr = 32 * kWaves;  // query rows per workgroup
+constexpr int kBc = 64;           // keys per tile
+constexpr int kKSlots = 3;        // K tiles resident or in flight
+constexpr int kVSlots = 3;        // row-major V tiles resident or in flight
+constexpr int kTSlots = 2;        // transposed V tiles
+
+// LDS row i of a K tile holds key sigma(i) of the tile (bits 2 and 3 swapped).
+__device__ __forceinline__ int sigma(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+// LDS tile layouts.  Every tile is a sequence of 256-byte blocks; a block holds
+// one 16-byte chunk of 16 consecutive rows, and block (row / 16, chunk) sits at
+// index (row / 16) * chunks_per_row + chunk.
+//  * K (64 rows x D) and V^T (D rows x 64 keys): an operand read of 16 lanes
+//    (16 consecutive rows, one chunk) covers one whole block, so every read is
+//    free of bank conflicts without any swizzle, and each lane's address is one
+//    base register plus an immediate that depends on (block row, chunk) only.
+//  * V staging (64 rows x D, read by ds_read_b64_tr_b16): the 16-byte slot of
+//    row r within its block is (r % 16) ^ (4 * (chunk % 4)), which spreads the
+//    4 rows x 4 chunks read by one half wave over 16 distinct bank groups.
+// One copy instruction of a wave fills 1 KB = 4 consecutive blocks, i.e. 16 rows
+// x 4 chunks (64 contiguous bytes of each of 16 rows in global memory).
+template <int CPR> __device__ __forceinline__ uint32_t k_byte(int row, int chunk) {
+  return (uint32_t)((((row >> 4) * CPR + chunk) << 8) + ((row & 15) << 4));
+}
+template <int CPR> __device__ __forceinline__ uint32_t vs_byte(int row, int chunk) {
+  return (uint32_t)((((row >> 4) * CPR + chunk) << 8) + ((((row & 15) ^ (4 * (chunk & 3)))) << 4));
+}
+
+template <int kDType, int D, bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
+  typedef Elem<kDType> E;
+  typedef typename E::V8 V8;
+  constexpr int CPR = D / 8;                          // 16-byte chunks per K/V row
+  constexpr int KS = D / 16;                          // k-steps of S = K Q^T
+  constexpr int DB = D / 32;                          // 32-wide output column blocks
+  constexpr int kTile = kBc * D;                      // elements of one K, V or V^T tile
+  constexpr int kLoads = kBc * CPR / (64 * kWaves);   // copy instructions per wave per tensor
+  constexpr int kRowStep = 4 * 16 * kWaves / CPR;     // rows covered by one instruction of all waves
+  constexpr float kNegInf = -__builtin_huge_valf();
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(kLoads >= 1 && kLoads * 64 * kWaves == kBc * CPR, "tile copy split");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t smem_[(kKSlots + kVSlots + kTSlots) * kTile];
+  FA2_LDS uint16_t* const sK = (FA2_LDS uint16_t*)smem_;
+  FA2_LDS uint16_t* const sVs = sK + kKSlots * kTile;
+  FA2_LDS uint16_t* const sVt = sVs + kVSlots * kTile;
+
+  const int N = a.N;
+  int bh, qtile;
+  wg_to_tile(a, kCausal, bh, qtile);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: products first in each step, 1: softmax first
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int col = lane & 31;
+  const int q_row0 = qtile * kBr + wave * 32;
+  const int my_q = q_row0 + col;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const uint16_t* __restrict__ kh = a.k + head_off;
+  const uint16_t* __restrict__ vh = a.v + head_off;
+
+  // Copy layout: instruction t of this wave fills the 1 KB at q = t*kWaves +
+  // wave, i.e. blocks 4q..4q+3: rows 16*(4q / CPR) + 0..15 of chunks
+  // (4q % CPR) + 0..3.  Lane i takes block 4q + i/16 and slot i % 16.  From one
+  // t to the next only the block row moves (by kRowStep rows), so each lane
+  // keeps one global byte offset per tensor and t and the tile move a
+  // wave-uniform base.
+  const int cch = (4 * wave) % CPR + (lane >> 4);     // chunk this lane copies
+  const int crow = 16 * ((4 * wave) / CPR);          // first row of its block (t = 0)
+  const int kr = crow + (lane & 15);                  // K: LDS row; holds key sigma(kr)
+  const int vr = crow + ((lane & 15) ^ (4 * (cch & 3)));  // V: row that lands in slot lane & 15
+  const uint32_t voffK = (uint32_t)((sigma(kr) * D + cch * 8) * 2);
+  const uint32_t voffV = (uint32_t)((vr * D + cch * 8) * 2);
+
+  const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
+  const int nt = (kv_end + kBc - 1) / kBc;
+
+  auto issue_tile = [&](int j, int slot) __attribute__((always_inline)) {
+    const int kv0 = j * kBc;
+    FA2_LDS uint16_t* dk = sK + slot * kTile;
+    FA2_LDS uint16_t* dv = sVs + slot * kTile;
+    if (kv0 + kBc <= N) {
+      const char* kb = (const char*)(kh + (int64_t)kv0 * D);
+      const char* vb = (const char*)(vh + (int64_t)kv0 * D);
+#pragma unroll
+      for (int t = 0; t < kLoads; ++t) {
+        dma16_sbase(kb + t * kRowStep * D * 2, voffK, dk + (t * kWaves + wave) * 64 * 8);
+        dma16_sbase(vb + t * kRowStep * D * 2, voffV, dv + (t * kWaves + wave) * 64 * 8);
+      }
+    } else {
+      // Ragged last tile: rows past N re-read row N-1 (their scores are masked).
+#pragma unroll
+      for (int t = 0; t < kLoads; ++t) {
+        const int gk = min(kv0 + sigma(kr + t * kRowStep), N - 1);
+        const int gv = min(kv0 + vr + t * kRowStep, N - 1);
+        dma16(kh + (int64_t)gk * D + cch * 8, dk + (t * kWaves + wave) * 64 * 8);
+        dma16(vh + (int64_t)gv * D + cch * 8, dv + (t * kWaves + wave) * 64 * 8);
+      }
+    }
+  };
+
+  // The V^T slot that the first product phase reads (with all-zero weights)
+  // must hold finite values: fill it with zeros.
+  {
+    FA2_LDS u32x4* z = (FA2_LDS u32x4*)(sVt + ((kTSlots - 1) % kTSlots) * kTile);
+#pragma unroll
+    for (int i = tid; i < kTile / 8; i += kThreads) z[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Tiles 0 and 1 start streaming first (tile 1 repeats tile 0 if there is
+  // only one: every step keeps the same number of copies in flight).
+  issue_tile(0, 0);
+  issue_tile(min(1, nt - 1), 1);
+
+  // Q fragments (B operand of S^T = K Q^T), kept in registers for the whole
+  // loop.  Consumed here so the compiler's wait for them stays out of the loop.
+  V8 qf[KS];
+  {
+    const uint16_t* qp = a.q + head_off + (int64_t)min(my_q, N - 1) * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(qp + 16 * ks));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m_run = kNegInf;  // reference max of this lane's query row, log2 units
+  float l_part = 0.f;     // this lane's share of the row sum
+  f32x16 s[2];            // scores of one tile, between its S and softmax phases
+  uint32_t pk[2][8];      // probabilities of one tile, between softmax and P.V
+
+  auto wave_active = [&](int j) __attribute__((always_inline)) { return !kCausal || j * kBc <= q_row0 + 31; };
+
+  // Operand addresses: lane (hl, col) reads row 32*kb + col, chunk 2*ks + hl of
+  // K, and column 32*db + col, chunk 2*c + hl of V^T.
+  const uint32_t kaddr0 = k_byte<CPR>(col, hl);
+  const uint32_t taddr0 = k_byte<kBc / 8>(col, hl);
+
+  // The products of one phase, P.V of tile jp (if jp >= 0) then S = K Q^T of
+  // tile js (if js >= 0), run as one pipeline over their operand fragments:
+  // loads run kPipe fragments ahead of the MFMAs that use them, across the
+  // boundary between the two products, and the scheduling fences keep the
+  // compiler from hoisting every load of the phase (a register quad each).
+  // The copy of a future K/V tile is issued from the middle of the pipeline so
+  // that its address work hides under the MFMAs.  Consecutive MFMAs use
+  // different accumulators (4 output blocks, 2 score blocks).
+  constexpr int kPipe = 4;
+  constexpr int kNpv = (kBc / 16) * DB;  // P.V fragments: i -> (c = i / DB, db = i % DB)
+  constexpr int kNs = 2 * KS;            // S fragments: i -> (ks = i / 2, kb = i % 2)
+  // One product phase: O^T += V^T P^T for the V^T tile in slot tslot, then
+  // S^T = K Q^T for the K tile in slot kslot.  Both always run: a step without a
+  // P.V term has all-zero probabilities (pk), and scores nobody needs are simply
+  // not used, which keeps a single code path (and register allocation) for the
+  // loop.  The copy of a future K/V tile is issued from inside the pipeline.
+  auto mfma_phase = [&](int tslot, int kslot, int copy_tile, int copy_slot) __attribute__((always_inline)) {
+    const uint32_t tbase = (uint32_t)(size_t)(sVt + tslot * kTile) + taddr0;
+    const uint32_t kbase = (uint32_t)(size_t)(sK + kslot * kTile) + kaddr0;
+    auto load = [&](int i) __attribute__((always_inline)) {
+      uint32_t ad;
+      if (i < kNpv) ad = tbase + (uint32_t)((((i % DB) * 2 * (kBc / 8)) + 2 * (i / DB)) << 8);
+      else ad = kbase + (uint32_t)(((((i - kNpv) & 1) * 2 * CPR) + 2 * ((i - kNpv) >> 1)) << 8);
+      return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(size_t)ad);
+    };
+    V8 fr[kPipe];
+#pragma unroll
+    for (int i = 0; i < kPipe; ++i) fr[i] = load(i);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < kNpv + kNs; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < kNpv) {
+        const int c = i / DB;
+        const u32x4 bw = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1], pk[c >> 1][4 * (c & 1) + 2],
+                          pk[c >> 1][4 * (c & 1) + 3]};
+        o[i % DB] = E::mfma(fr[i % kPipe], __builtin_bit_cast(V8, bw), o[i % DB]);
+      } else {
+        const int k = i - kNpv;
+        s[k & 1] = E::mfma(fr[i % kPipe], qf[k >> 1], s[k & 1]);
+      }
+      if (i + kPipe < kNpv + kNs) fr[i % kPipe] = load(i + kPipe);
+      if (i == 6 && copy_tile >= 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_tile(copy_tile, copy_slot);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto zero_pk = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) pk[kb][r] = 0u;
+  };
+
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int kv0 = j * kBc;
+    const bool need_mask = (kv0 + kBc > N) || (kCausal && kv0 + kBc - 1 > q_row0);
+    float mul = a.c2;
+    if (need_mask || !(a.c2 > 0.f)) {
+      // Scale first, then mask: -inf for keys past N or after the query.  The
+      // key of element (kb, r) is kv0 + 8*hl + off with a constant off, so each
+      // test compares one per-lane value with an immediate.
+      const int rel_n = kv0 + 8 * hl - N;     // key >= N  <=>  rel_n + off >= 0
+      const int rel_q = kv0 + 8 * hl - my_q;  // key > q   <=>  rel_q + off > 0
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * kb + 16 * (r >> 3) + (r & 7);
+          const bool masked = rel_n >= -off || (kCausal && rel_q > -off);
+          const float t = s[kb][r] * a.c2;
+          s[kb][r] = masked ? kNegInf : t;
+        }
+      }
+      mul = 1.f;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_pair32(mx);
+    const float m_tile = mx * mul;
+    const bool need = m_tile > m_run + kTau;
+    if (__any(need)) {
+      const float m_new = need ? m_tile : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], mul, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], mul, -m_use));
+        pk[kb][r >> 1] = E::pack2(p0, p1);
+        ls[(r >> 1) & 3] += p0 + p1;
+      }
+    }
+    l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
+  // Half of V tile j (this group's share), staging -> V^T.  Wave w handles keys
+  // 8w .. 8w+7 (group 0 the first 32 keys, group 1 the rest).  For each span of
+  // 64 columns, two ds_read_b64_tr_b16 give lane (g, L) keys 8w + 0..3 and
+  // 8w + 4..7 of column 16g + L, which one ds_write_b128 stores as a whole
+  // 16-byte slot (each 16 lanes write 256 contiguous bytes).
+  const int tg = lane >> 4;
+  const int tl = lane & 15;
+  const int tch = 2 * tg + ((tl & 3) >> 1);  // source chunk within a span
+  const uint32_t trd0 = vs_byte<CPR>(8 * wave + (tl >> 2), tch) + 8 * (tl & 1);
+  const uint32_t trd1 = vs_byte<CPR>(8 * wave + 4 + (tl >> 2), tch) + 8 * (tl & 1);
+  const uint32_t twr0 = k_byte<kBc / 8>(16 * tg + tl, wave);
+  u32x2 tv[D / 64][2];  // transposed V data between its read and its write
+  auto transpose_read = [&](int j) __attribute__((always_inline)) {
+    const uint32_t src = (uint32_t)(size_t)(sVs + (j % kVSlots) * kTile);
+#pragma unroll
+    for (int dq = 0; dq < D / 64; ++dq) {
+      const uint32_t so = (uint32_t)(dq * 8 * 256);  // chunk + 8 per span
+      tv[dq][0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(src + trd0 + so)));
+      tv[dq][1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(src + trd1 + so)));
+    }
+  };
+  auto transpose_write = [&](int j) __attribute__((always_inline)) {
+    const uint32_t dst = (uint32_t)(size_t)(sVt + (j % kTSlots) * kTile) + twr0;
+#pragma unroll
+    for (int dq = 0; dq < D / 64; ++dq)
+      *(FA2_LDS u32x4*)(size_t)(dst + (uint32_t)(dq * 32 * 256)) = u32x4{tv[dq][0][0], tv[dq][0][1], tv[dq][1][0], tv[dq][1][1]};
+  };
+
+  // Step st: both groups meet at the two barriers; in between, group 0 runs
+  // [P.V(st-1), S(st)] then [softmax(st), transpose half of V(st)], and group 1
+  // runs [softmax(st-1), transpose half of V(st)] then [P.V(st-1), S(st)].
+  // Each wave copies its share of tile st+2 from inside its product phase:
+  // tile st+2 goes to slot (st+2) % 3, which held tile st-1 (no longer read);
+  // past the last tile the copy repeats tile nt-1 into that free slot, so that
+  // every step keeps the same number of copies in flight.  Each group has its
+  // own copy of the loop so that the compiler sees which registers stay live
+  // across steps (pk for group 0, s for group 1); both copies execute the same
+  // barriers in the same order.
+  auto copy_tile_of = [&](int st) __attribute__((always_inline)) { return st < nt ? min(st + 2, nt - 1) : -1; };
+  zero_pk();
+  if (grp == 0) {
+    for (int st = 0; st <= nt; ++st) {
+      // Tile st has landed for every wave (tile st+1 may still be in flight),
+      // and every LDS access of the previous step is complete.
+      wait_vm_lds_barrier<2 * kLoads>();
+      mfma_phase((st + kTSlots - 1) % kTSlots, st % kKSlots, copy_tile_of(st), (st + 2) % kKSlots);
+      lds_done_barrier();
+      if (st < nt) transpose_read(st);
+      if (st < nt && wave_active(st)) softmax(st);
+      else zero_pk();
+      if (st < nt) transpose_write(st);
+    }
+  } else {
+    for (int st = 0; st <= nt; ++st) {
+      wait_vm_lds_barrier<2 * kLoads>();
+      if (st < nt) transpose_read(st);
+      if (st >= 1 && wave_active(st - 1)) softmax(st - 1);
+      else zero_pk();
+      if (st < nt) transpose_write(st);
+      lds_done_barrier();
+      mfma_phase((st + kTSlots - 1) % kTSlots, st % kKSlots, copy_tile_of(st), (st + 2) % kKSlots);
+    }
+  }
+  // No LDS write may still be in flight when the workgroup retires.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue: one division per row, logsumexp in natural-log units.
+  const float l_row = sum_pair32(l_part);
+  const float inv = 1.f / l_row;
+  if (my_q < N) {
+    uint16_t* op = a.o + head_off + (int64_t)my_q * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = 32 * db + 8 * r4 + 4 * hl;
+        const u32x2 wv = {E::pack2(o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv),
+                          E::pack2(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv)};
+        *(u32x2*)(op + dim) = wv;
+      }
+    }
+    if (hl == 0) a.lse[(int64_t)bh * N + my_q] = (m_run + __log2f(l_row)) * kLn2;
+  }
+}
+
+}  // namespace w8
+}  // namespace fa2

@@ -18,7 +18,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import re
 import sys
@@ -107,8 +106,13 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
             flop += 4.0 * w.d * keys
         return flop, secs
 
-    _, t_cal = run(64, 1)
-    total_rows = max(64, int(64 * target_s / max(t_cal, 1e-3)))
+    # Calibrate on enough rows to give every thread work (the oracle hands out
+    # rows in blocks of 64), then size the sample to about target_s seconds.
+    cal_rows = min(w.N, 64 * threads)
+    f_cal, t_cal = run(cal_rows, 1)
+    rate = f_cal / max(t_cal, 1e-6)                       # FLOP/s of the oracle
+    flop_per_row = f_cal / cal_rows
+    total_rows = max(cal_rows, int(rate * target_s / flop_per_row))
     rows_per_head = min(w.N, total_rows)
     n_heads = max(1, min(len(heads), total_rows // rows_per_head))
     flop, secs = run(rows_per_head, n_heads)
@@ -127,6 +131,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--min-warmup-ms", type=float, default=300.0,
+                    help="extra untimed steps until the warm-up has lasted this long (clock ramp-up)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the oracle sample")
@@ -172,6 +178,16 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The engine clock ramps up over the first tens of milliseconds of MFMA load;
+    # keep running untimed steps until the warm-up has lasted min_warmup_ms so the
+    # timed steps see the steady clock (the count is reported in the JSON line).
+    extra = 0
+    t_w0 = time.perf_counter()
+    while (time.perf_counter() - t_w0) * 1e3 < args.min_warmup_ms:
+        for _ in range(5):
+            step()
+        extra += 5
+        torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -201,6 +217,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_warmup_steps": extra,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -3,8 +3,8 @@
 Tolerances: max |dO| <= 2e-3 for fp16 and <= 1e-2 for bf16, max |dL| <= 1e-3,
 taken over every compared element.  Small problems (several tiles and a ragged
 tail) are compared in full; the named workloads run at full size in the same
-launch configuration the benchmark times and are compared on sampled rows that
-the oracle computes one by one.
+launch configuration the benchmark times and are compared on whole (batch,
+head) slices plus sampled rows that the oracle computes one by one.
 """
 import math
 
@@ -110,7 +110,7 @@ def test_parity_far_max_growth():
         _compare(o, lse, o_ref, l_ref, torch.bfloat16, f"max growth causal={causal}")
 
 
-# --- named workloads at full size, sampled rows -------------------------------------
+# --- named workloads at full size ------------------------------------------------------
 
 def _sample_rows(N, rng, n_random=40):
     fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, N // 2, N - 129, N - 128, N - 65, N - 64, N - 2, N - 1]
@@ -120,15 +120,21 @@ def _sample_rows(N, rng, n_random=40):
 
 
 @pytest.mark.parametrize("name", [n for n in WORKLOADS if n != "tiny_d64"])
-def test_parity_workload_full_size_sampled(name):
+def test_parity_workload_full_size(name):
+    """Full-size workload in the benchmark's launch configuration: the first and
+    the last (batch, head) slices are compared on every row, two more slices on
+    sampled rows the oracle computes one by one."""
     w = WORKLOADS[name]
     q, k, v = workload_inputs(w, seed=0)
     _log(f"workload {name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
     o, lse = _gpu_run(q, k, v, w.causal, w.scale)
+    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+        o_ref, l_ref = oracle.attention_f64(q[b, h].double().numpy(), k[b, h].double().numpy(),
+                                            v[b, h].double().numpy(), w.causal, _f32(w.scale))
+        _compare(o[b, h], lse[b, h], o_ref, l_ref, w.torch_dtype, f"(b={b},h={h}) all {w.N} rows")
     rng = np.random.default_rng(0)
-    heads = sorted({(0, 0), (w.B - 1, w.H - 1)} | {(int(rng.integers(w.B)), int(rng.integers(w.H)))
-                                                    for _ in range(2)})
-    for (b, h) in heads:
+    for _ in range(2):
+        b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
         rows = _sample_rows(w.N, rng)
         o_ref, l_ref = oracle.attention_rows_f64(q[b, h].double().numpy(), k[b, h].double().numpy(),
                                                  v[b, h].double().numpy(), rows, w.causal, _f32(w.scale))

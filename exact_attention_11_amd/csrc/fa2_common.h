@@ -23,6 +23,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // when a tile's row max exceeds it by more than this, so unnormalised weights
 // stay below 2^kTau (far inside the fp16 range).
 constexpr float kTau = 8.0f;
+// A lane's share of a tile's row sum at most this bounds each of its weights by
+// 2^kTau as well (the weights are non-negative).
+constexpr float kSumCap = 256.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 struct FwdArgs {
@@ -111,16 +114,27 @@ __device__ __forceinline__ float sum_pair32(float x) {
 }
 
 // Workgroup id -> (head, query tile).  Consecutive dispatch ids go round-robin
-// over the 8 XCDs; regroup them so that each XCD walks a contiguous range of
-// heads (its L2 then serves that head's K/V to every query tile).  Under a
-// causal mask the query tiles of a head are issued heaviest (last) first.
+// over the 8 XCDs.
+//  * Without a mask every tile costs the same: regroup the ids so that each XCD
+//    walks a contiguous range of heads (its L2 then serves that head's K/V to
+//    every query tile).
+//  * Under a causal mask tile cost grows with the tile index: issue all heads'
+//    last (heaviest) query tiles first, then the next ones, so every XCD's queue
+//    runs heaviest first; head h lands on XCD h % 8 whenever the head count is a
+//    multiple of 8, which keeps each head's K/V in one L2.
 __device__ __forceinline__ void wg_to_tile(const FwdArgs& a, bool causal, int& bh, int& qtile) {
   const int w = blockIdx.x;
+  const int n_bh = a.n_wg / a.n_qtiles;
+  if (causal) {
+    const int level = w / n_bh;
+    bh = w - level * n_bh;
+    qtile = a.n_qtiles - 1 - level;
+    return;
+  }
   int sidx = w;
   if ((a.n_wg & 7) == 0) sidx = (w & 7) * (a.n_wg >> 3) + (w >> 3);
   bh = sidx / a.n_qtiles;
-  const int it = sidx - bh * a.n_qtiles;
-  qtile = causal ? (a.n_qtiles - 1 - it) : it;
+  qtile = sidx - bh * a.n_qtiles;
 }
 
 }  // namespace fa2

@@ -42,9 +42,10 @@
 //  * Softmax.  exp2 with the multiplier and log2(e) folded into one FMA; the
 //    row sum adds the fp32 weights with plain adds (v_dot2 would be cheaper in
 //    instructions, but it stalls behind the other wave's MFMAs on the same
-//    SIMD); the reference max of a row moves only
-//    when a tile's row max exceeds it by more than kTau, so the O rescale is
-//    rare; the result is the same mathematically.
+//    SIMD).  The reference max of a row moves only when a weight would exceed
+//    2^kTau, so the O rescale is rare and the steady state computes no row max
+//    at all (the weights' own sum shows that none is too large); the result is
+//    the same mathematically, since O and l share the reference.
 //  * Scheduling.  Workgroups are remapped so each XCD walks a contiguous range
 //    of heads (L2 reuse of K/V); causal query tiles go heaviest first.
 #pragma once
@@ -223,6 +224,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
       else ad = kbase + (uint32_t)(((((i - kNpv) & 1) * 2 * CPR) + 2 * ((i - kNpv) >> 1)) << 8);
       return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(size_t)ad);
     };
+    // The wave running products is preferred at instruction issue so that
+    // its MFMAs are not held back by the other wave's softmax on the SIMD.
+    __builtin_amdgcn_s_setprio(2);
     V8 fr[kPipe];
 #pragma unroll
     for (int i = 0; i < kPipe; ++i) fr[i] = load(i);
@@ -247,6 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   auto zero_pk = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -255,6 +260,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
       for (int r = 0; r < 8; ++r) pk[kb][r] = 0u;
   };
 
+  // Softmax of tile j into pk, updating the row statistics.  The reference max
+  // m_run moves only when some weight would exceed 2^kTau, and a lane's share of
+  // the tile's row sum bounds every weight it holds, so the steady state needs no
+  // row max: the weights are formed against the current reference and accepted
+  // when every lane's share is at most kSumCap (an overflowed exp fails the test
+  // too).  Otherwise (and always on the first tile) the tile's row max decides
+  // whether the reference moves, O and l are rescaled by 2^(old - new), and the
+  // weights are formed again.
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int kv0 = j * kBc;
     const bool need_mask = (kv0 + kBc > N) || (kCausal && kv0 + kBc - 1 > q_row0);
@@ -277,37 +290,51 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
       }
       mul = 1.f;
     }
-    float mx = s[0][0];
+    // Weights 2^(s*mul - m) of this lane's 32 scores, rounded into pk; returns
+    // their fp32 sum (the unrounded weights).
+    auto weights = [&](float m) __attribute__((always_inline)) {
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_pair32(mx);
-    const float m_tile = mx * mul;
-    const bool need = m_tile > m_run + kTau;
-    if (__any(need)) {
-      const float m_new = need ? m_tile : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_run = m_new;
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], mul, -m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], mul, -m));
+          pk[kb][r >> 1] = E::pack2(p0, p1);
+          ls[(r >> 1) & 3] += p0 + p1;
+        }
+      }
+      return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    float lsum = 0.f;
+    bool accepted = false;
+    if (j > 0) {
+      lsum = weights(m_run);
+      accepted = __all(lsum <= kSumCap);
     }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    if (!accepted) {
+      // Row max of the scaled scores; key 0 is never masked, so it is finite
+      // on the first tile.
+      float mx = s[0][0] * mul;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], mul, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], mul, -m_use));
-        pk[kb][r >> 1] = E::pack2(p0, p1);
-        ls[(r >> 1) & 3] += p0 + p1;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r] * mul);
+      const float m_tile = max_pair32(mx);
+      const bool need = m_tile > m_run + kTau;
+      if (j == 0 || __any(need)) {
+        const float m_new = need ? m_tile : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_run = m_new;
+        lsum = weights(m_run);
       }
     }
-    l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    l_part += lsum;
   };
 
   // Half of V tile j (this group's share), staging -> V^T.  Wave w handles keys
@@ -350,13 +377,20 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   // barriers in the same order.
   auto copy_tile_of = [&](int st) __attribute__((always_inline)) { return st < nt ? min(st + 2, nt - 1) : -1; };
   zero_pk();
+  // The scheduling fences keep each phase's work on its own side of the
+  // barriers (register-only arithmetic could otherwise move across them and
+  // unbalance the two phases).
   if (grp == 0) {
     for (int st = 0; st <= nt; ++st) {
       // Tile st has landed for every wave (tile st+1 may still be in flight),
       // and every LDS access of the previous step is complete.
+      __builtin_amdgcn_sched_barrier(0);
       wait_vm_lds_barrier<2 * kLoads>();
+      __builtin_amdgcn_sched_barrier(0);
       mfma_phase((st + kTSlots - 1) % kTSlots, st % kKSlots, copy_tile_of(st), (st + 2) % kKSlots);
+      __builtin_amdgcn_sched_barrier(0);
       lds_done_barrier();
+      __builtin_amdgcn_sched_barrier(0);
       if (st < nt) transpose_read(st);
       if (st < nt && wave_active(st)) softmax(st);
       else zero_pk();
@@ -364,12 +398,16 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
     }
   } else {
     for (int st = 0; st <= nt; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
       wait_vm_lds_barrier<2 * kLoads>();
+      __builtin_amdgcn_sched_barrier(0);
       if (st < nt) transpose_read(st);
       if (st >= 1 && wave_active(st - 1)) softmax(st - 1);
       else zero_pk();
       if (st < nt) transpose_write(st);
+      __builtin_amdgcn_sched_barrier(0);
       lds_done_barrier();
+      __builtin_amdgcn_sched_barrier(0);
       mfma_phase((st + kTSlots - 1) % kTSlots, st % kKSlots, copy_tile_of(st), (st + 2) % kKSlots);
     }
   }

@@ -94,20 +94,68 @@ def test_parity_unusual_scales(scale, causal):
     _full_parity(1, 2, 300, 128, torch.float16, causal, scale=scale, seed=7)
 
 
-def test_parity_far_max_growth():
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
+def test_parity_far_max_growth(dtype, d):
     """Scores whose row max climbs tile after tile (keys sorted by score), which
     forces the running-max rescale on many tiles."""
-    N, d = 700, 64
-    q, k, v = make_qkv(1, 1, N, d, torch.bfloat16, "normal", 3)
+    N = 700
+    q, k, v = make_qkv(1, 1, N, d, dtype, "normal", 3)
     q = torch.zeros_like(q)
     q[..., 0] = 1.0
     k = torch.zeros_like(k)
-    k[0, 0, :, 0] = torch.linspace(-30.0, 30.0, N).to(torch.bfloat16)
+    k[0, 0, :, 0] = torch.linspace(-30.0, 30.0, N).to(dtype)
     for causal in (False, True):
+        _log(f"case max growth {dtype} d={d} causal={causal}")
         o, lse = _gpu_run(q, k, v, causal, 1.0)
         o_ref, l_ref = oracle.attention_f64(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal,
                                             1.0)
-        _compare(o, lse, o_ref, l_ref, torch.bfloat16, f"max growth causal={causal}")
+        _compare(o, lse, o_ref, l_ref, dtype, f"max growth causal={causal}")
+
+
+@pytest.mark.parametrize("pattern", ["overflow_jump", "finite_jump", "plateau", "late_dip"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
+def test_parity_reference_moves(dtype, d, pattern):
+    """Score layouts aimed at each way a key tile can meet the row's reference
+    max: a later score so far above it that its weight overflows fp32
+    (overflow_jump), one far above it but finite (finite_jump), a whole tile of
+    scores just under the rescale threshold, whose weights add up past any
+    small bound while none is large (plateau), and tiles far below the first
+    one (late_dip).  Every row sees the same scores (q = e0, scale 1), so the
+    layout is exact for all rows; the causal runs cut it at each row.
+
+    V is scaled by 1/4 (exact) so that |O| stays near 1, where the absolute
+    tolerances apply: a single dominant weight can sit anywhere in (1, 2^8] and
+    keeps its rounding to the input type (2^-9 relative in bf16), so the error
+    of O grows with |v| on such rows."""
+    N = 320
+    q, k, v = make_qkv(1, 1, N, d, dtype, "normal", 11)
+    v = v * 0.25
+    q = torch.zeros_like(q)
+    q[..., 0] = 1.0
+    k = torch.zeros_like(k)
+    sc = torch.zeros(N)
+    if pattern == "overflow_jump":
+        sc[100] = 120.0      # 2^(120 log2 e) overflows fp32
+        sc[250] = 240.0
+    elif pattern == "finite_jump":
+        sc[70] = 40.0
+        sc[200] = 60.0
+        sc[201] = 61.0
+    elif pattern == "plateau":
+        sc[64:192] = 5.0     # 7.2 log2 units over the first tile's max
+        sc[250:] = 10.0
+    else:
+        sc[:64] = 20.0
+        sc[64:] = -20.0
+    k[0, 0, :, 0] = sc.to(dtype)
+    for causal in (False, True):
+        _log(f"case reference moves {pattern} {dtype} d={d} causal={causal}")
+        o, lse = _gpu_run(q, k, v, causal, 1.0)
+        o_ref, l_ref = oracle.attention_f64(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal,
+                                            1.0)
+        _compare(o, lse, o_ref, l_ref, dtype, f"{pattern} causal={causal}")
 
 
 # --- named workloads at full size ------------------------------------------------------

@@ -96,6 +96,14 @@ __device__ __forceinline__ void lds_done_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The value itself, computed into a VGPR the compiler cannot see through: the
+// addresses derived from it stay "base + immediate offset" instead of being
+// re-associated into one register (and one add per step) per access.
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // v_permlane32_swap exchanges the upper half of its first operand with the
 // lower half of its second.  With x in both, one result holds this lane's own
 // value and the other the value of lane l ^ 32 (which one depends on the half),

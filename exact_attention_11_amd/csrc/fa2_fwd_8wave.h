@@ -216,8 +216,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   // not used, which keeps a single code path (and register allocation) for the
   // loop.  The copy of a future K/V tile is issued from inside the pipeline.
   auto mfma_phase = [&](int tslot, int kslot, int copy_tile, int copy_slot) __attribute__((always_inline)) {
-    const uint32_t tbase = (uint32_t)(size_t)(sVt + tslot * kTile) + taddr0;
-    const uint32_t kbase = (uint32_t)(size_t)(sK + kslot * kTile) + kaddr0;
+    // One base register per operand; every fragment address is that base plus
+    // an immediate offset.
+    const uint32_t tbase = opaque_vgpr((uint32_t)(size_t)(sVt + tslot * kTile) + taddr0);
+    const uint32_t kbase = opaque_vgpr((uint32_t)(size_t)(sK + kslot * kTile) + kaddr0);
     auto load = [&](int i) __attribute__((always_inline)) {
       uint32_t ad;
       if (i < kNpv) ad = tbase + (uint32_t)((((i % DB) * 2 * (kBc / 8)) + 2 * (i / DB)) << 8);
@@ -272,37 +274,47 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
     const int kv0 = j * kBc;
     const bool need_mask = (kv0 + kBc > N) || (kCausal && kv0 + kBc - 1 > q_row0);
     float mul = a.c2;
-    if (need_mask || !(a.c2 > 0.f)) {
-      // Scale first, then mask: -inf for keys past N or after the query.  The
-      // key of element (kb, r) is kv0 + 8*hl + off with a constant off, so each
-      // test compares one per-lane value with an immediate.
-      const int rel_n = kv0 + 8 * hl - N;     // key >= N  <=>  rel_n + off >= 0
-      const int rel_q = kv0 + 8 * hl - my_q;  // key > q   <=>  rel_q + off > 0
+    if (need_mask) {
+      // Key of element (kb, r) = kv0 + 8*hl + off with a constant off; it is
+      // allowed iff off < lim (key < N, and key <= query under the causal mask).
+      const int base = kv0 + 8 * hl;
+      int lim = N - base;
+      if (kCausal) lim = min(lim, my_q + 1 - base);
+      if (a.c2 > 0.f) {
+        // -inf times a positive multiplier stays -inf: mask the raw scores.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 32 * kb + 16 * (r >> 3) + (r & 7);
-          const bool masked = rel_n >= -off || (kCausal && rel_q > -off);
-          const float t = s[kb][r] * a.c2;
-          s[kb][r] = masked ? kNegInf : t;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * kb + 16 * (r >> 3) + (r & 7);
+            s[kb][r] = off < lim ? s[kb][r] : kNegInf;
+          }
+      } else {
+        // Scale first, then mask.
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * kb + 16 * (r >> 3) + (r & 7);
+            const float t = s[kb][r] * a.c2;
+            s[kb][r] = off < lim ? t : kNegInf;
+          }
+        mul = 1.f;
       }
-      mul = 1.f;
     }
     // Weights 2^(s*mul - m) of this lane's 32 scores, rounded into pk; returns
-    // their fp32 sum (the unrounded weights).
+    // their fp32 sum (the unrounded weights), formed with 31 adds in four
+    // independent chains.
     auto weights = [&](float m) __attribute__((always_inline)) {
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      float ls[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], mul, -m));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], mul, -m));
-          pk[kb][r >> 1] = E::pack2(p0, p1);
-          ls[(r >> 1) & 3] += p0 + p1;
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int kb = e >> 3, r = 2 * (e & 7);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], mul, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], mul, -m));
+        pk[kb][r >> 1] = E::pack2(p0, p1);
+        if (e < 4) ls[e] = p0 + p1;
+        else ls[e & 3] += p0 + p1;
       }
       return (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
@@ -351,15 +363,16 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   u32x2 tv[D / 64][2];  // transposed V data between its read and its write
   auto transpose_read = [&](int j) __attribute__((always_inline)) {
     const uint32_t src = (uint32_t)(size_t)(sVs + (j % kVSlots) * kTile);
+    const uint32_t a0 = opaque_vgpr(src + trd0), a1 = opaque_vgpr(src + trd1);
 #pragma unroll
     for (int dq = 0; dq < D / 64; ++dq) {
       const uint32_t so = (uint32_t)(dq * 8 * 256);  // chunk + 8 per span
-      tv[dq][0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(src + trd0 + so)));
-      tv[dq][1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(src + trd1 + so)));
+      tv[dq][0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(a0 + so)));
+      tv[dq][1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(a1 + so)));
     }
   };
   auto transpose_write = [&](int j) __attribute__((always_inline)) {
-    const uint32_t dst = (uint32_t)(size_t)(sVt + (j % kTSlots) * kTile) + twr0;
+    const uint32_t dst = opaque_vgpr((uint32_t)(size_t)(sVt + (j % kTSlots) * kTile) + twr0);
 #pragma unroll
     for (int dq = 0; dq < D / 64; ++dq)
       *(FA2_LDS u32x4*)(size_t)(dst + (uint32_t)(dq * 32 * 256)) = u32x4{tv[dq][0][0], tv[dq][0][1], tv[dq][1][0], tv[dq][1][1]};

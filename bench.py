@@ -81,8 +81,9 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
     """Time the fp64 oracle on a strided sample of the workload's query rows.
 
     Rows are strided over the whole sequence, so the mix of causal row lengths
-    matches the full workload; heads are taken in order.  A 64-row run sizes the
-    sample to about ``target_s`` seconds of wall time.
+    matches the full workload.  A first (untimed) run on one head sizes the rows
+    per head; whole heads are then timed in order until the sample has taken
+    about ``target_s`` seconds (or the heads run out).
     """
     import numpy as np
 
@@ -92,30 +93,31 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
     scale = float(np.float32(w.scale))
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
 
-    def run(rows_per_head: int, n_heads: int):
-        flop, secs = 0.0, 0.0
+    def run_head(i: int, rows_per_head: int):
         stride = max(1, w.N // rows_per_head)
-        for i in range(n_heads):
-            b, h = heads[i]
-            qq, kk, vv = (t[b, h].double().numpy() for t in (q, k, v))
-            rows = np.arange(i % stride, w.N, stride, dtype=np.int64)[:rows_per_head]
-            t0 = time.perf_counter()
-            oracle.attention_rows_f64(qq, kk, vv, rows, w.causal, scale, nthreads=threads)
-            secs += time.perf_counter() - t0
-            keys = float((rows + 1).sum()) if w.causal else float(len(rows)) * w.N
-            flop += 4.0 * w.d * keys
-        return flop, secs
+        b, h = heads[i]
+        qq, kk, vv = (t[b, h].double().numpy() for t in (q, k, v))
+        rows = np.arange(i % stride, w.N, stride, dtype=np.int64)[:rows_per_head]
+        t0 = time.perf_counter()
+        oracle.attention_rows_f64(qq, kk, vv, rows, w.causal, scale, nthreads=threads)
+        secs = time.perf_counter() - t0
+        keys = float((rows + 1).sum()) if w.causal else float(len(rows)) * w.N
+        return 4.0 * w.d * keys, secs
 
     # Calibrate on enough rows to give every thread work (the oracle hands out
-    # rows in blocks of 64), then size the sample to about target_s seconds.
+    # rows in blocks of 64); this run also warms the thread pool and is not
+    # counted.
     cal_rows = min(w.N, 64 * threads)
-    f_cal, t_cal = run(cal_rows, 1)
+    f_cal, t_cal = run_head(0, cal_rows)
     rate = f_cal / max(t_cal, 1e-6)                       # FLOP/s of the oracle
     flop_per_row = f_cal / cal_rows
-    total_rows = max(cal_rows, int(rate * target_s / flop_per_row))
-    rows_per_head = min(w.N, total_rows)
-    n_heads = max(1, min(len(heads), total_rows // rows_per_head))
-    flop, secs = run(rows_per_head, n_heads)
+    rows_per_head = min(w.N, max(cal_rows, int(rate * target_s / flop_per_row)))
+    flop, secs, n_heads = 0.0, 0.0, 0
+    while n_heads < len(heads) and secs < target_s:
+        f, t = run_head(n_heads, rows_per_head)
+        flop += f
+        secs += t
+        n_heads += 1
     return {
         "value": flop / secs / 1e12,
         "unit": "TFLOP/s",

@@ -122,27 +122,45 @@ __device__ __forceinline__ float sum_pair32(float x) {
 }
 
 // Workgroup id -> (head, query tile).  Consecutive dispatch ids go round-robin
-// over the 8 XCDs.
+// over the 8 XCDs (32 CUs and one L2 each on MI355X), so id w runs on XCD w % 8.
 //  * Without a mask every tile costs the same: regroup the ids so that each XCD
 //    walks a contiguous range of heads (its L2 then serves that head's K/V to
 //    every query tile).
-//  * Under a causal mask tile cost grows with the tile index: issue all heads'
-//    last (heaviest) query tiles first, then the next ones, so every XCD's queue
-//    runs heaviest first; head h lands on XCD h % 8 whenever the head count is a
-//    multiple of 8, which keeps each head's K/V in one L2.
+//  * Under a causal mask tile cost grows with the tile index.  When the head
+//    count is a multiple of 8, XCD x takes heads x, x + 8, ... in groups of g
+//    heads, g = 32 / (query tiles per head) (at least 1): inside a group the
+//    query tiles go heaviest first across the group's heads.  A group then
+//    fills about one round of the XCD's CUs, which keeps the concurrent
+//    workgroups on few heads (L2 reuse) while every CU's queue still runs
+//    heaviest first.  Otherwise all heads' heaviest tiles go first.
+constexpr int kCusPerXcd = 32;
 __device__ __forceinline__ void wg_to_tile(const FwdArgs& a, bool causal, int& bh, int& qtile) {
   const int w = blockIdx.x;
-  const int n_bh = a.n_wg / a.n_qtiles;
+  const int nq = a.n_qtiles;
+  const int n_bh = a.n_wg / nq;
   if (causal) {
-    const int level = w / n_bh;
-    bh = w - level * n_bh;
-    qtile = a.n_qtiles - 1 - level;
+    if ((n_bh & 7) == 0) {
+      const int x = w & 7, it = w >> 3;
+      const int hpx = n_bh >> 3;  // heads per XCD
+      int g = kCusPerXcd / nq;
+      g = g < 1 ? 1 : (g > hpx ? hpx : g);
+      const int grp = it / (g * nq);
+      const int r = it - grp * g * nq;
+      const int gg = min(g, hpx - grp * g);  // the last group may be smaller
+      const int level = r / gg;
+      bh = (grp * g + (r - level * gg)) * 8 + x;
+      qtile = nq - 1 - level;
+    } else {
+      const int level = w / n_bh;
+      bh = w - level * n_bh;
+      qtile = nq - 1 - level;
+    }
     return;
   }
   int sidx = w;
   if ((a.n_wg & 7) == 0) sidx = (w & 7) * (a.n_wg >> 3) + (w >> 3);
-  bh = sidx / a.n_qtiles;
-  qtile = sidx - bh * a.n_qtiles;
+  bh = sidx / nq;
+  qtile = sidx - bh * nq;
 }
 
 }  // namespace fa2

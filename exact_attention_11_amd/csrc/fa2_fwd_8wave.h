@@ -199,46 +199,65 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   const uint32_t kaddr0 = k_byte<CPR>(col, hl);
   const uint32_t taddr0 = k_byte<kBc / 8>(col, hl);
 
-  // The products of one phase, P.V of tile jp (if jp >= 0) then S = K Q^T of
-  // tile js (if js >= 0), run as one pipeline over their operand fragments:
-  // loads run kPipe fragments ahead of the MFMAs that use them, across the
-  // boundary between the two products, and the scheduling fences keep the
-  // compiler from hoisting every load of the phase (a register quad each).
-  // The copy of a future K/V tile is issued from the middle of the pipeline so
-  // that its address work hides under the MFMAs.  Consecutive MFMAs use
-  // different accumulators (4 output blocks, 2 score blocks).
+  // The products of one phase run as one pipeline over their operand
+  // fragments: loads run kPipe fragments ahead of the MFMAs that use them,
+  // across the boundary between the two products, and the scheduling fences
+  // keep the compiler from hoisting every load of the phase (a register quad
+  // each).  The copy of a future K/V tile is issued from the middle of the
+  // pipeline so that its address work hides under the MFMAs.  Consecutive MFMAs
+  // use different accumulators (4 output blocks, 2 score blocks).
+  //
+  // P.V runs first, over the key blocks of the V^T tile in the order 32-47,
+  // 48-63, 0-15, 16-31 (fragment f -> key block c = (f / DB + 2) % 4, output
+  // block f % DB).  Keys 32-63 of a V^T tile are written by group 1 before the
+  // middle barrier of the step that transposes it, so both groups may load the
+  // first kPipe fragments before the barrier that opens their product phase
+  // (prefetch): the barrier's wait then covers the load latency.
   constexpr int kPipe = 4;
-  constexpr int kNpv = (kBc / 16) * DB;  // P.V fragments: i -> (c = i / DB, db = i % DB)
-  constexpr int kNs = 2 * KS;            // S fragments: i -> (ks = i / 2, kb = i % 2)
+  constexpr int kNpv = (kBc / 16) * DB;  // P.V fragments
+  constexpr int kNs = 2 * KS;            // S fragments: f -> (ks = f / 2, kb = f % 2)
+  static_assert(kPipe <= 2 * DB, "prefetched fragments must lie in keys 32-63");
+  auto pv_c = [](int f) constexpr { return (f / DB + 2) % (kBc / 16); };
+  V8 fr[kPipe];
+  auto load_op = [&](uint32_t tbase, uint32_t kbase, int i) __attribute__((always_inline)) {
+    uint32_t ad;
+    if (i < kNpv) ad = tbase + (uint32_t)((((i % DB) * 2 * (kBc / 8)) + 2 * pv_c(i)) << 8);
+    else ad = kbase + (uint32_t)(((((i - kNpv) & 1) * 2 * CPR) + 2 * ((i - kNpv) >> 1)) << 8);
+    return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(size_t)ad);
+  };
+  auto tslot_base = [&](int tslot) __attribute__((always_inline)) {
+    // One base register per operand; every fragment address is that base plus
+    // an immediate offset.
+    return opaque_vgpr((uint32_t)(size_t)(sVt + tslot * kTile) + taddr0);
+  };
+  auto prefetch = [&](int tslot) __attribute__((always_inline)) {
+    const uint32_t tbase = tslot_base(tslot);
+#pragma unroll
+    for (int i = 0; i < kPipe; ++i) fr[i] = load_op(tbase, 0u, i);
+  };
   // One product phase: O^T += V^T P^T for the V^T tile in slot tslot, then
   // S^T = K Q^T for the K tile in slot kslot.  Both always run: a step without a
   // P.V term has all-zero probabilities (pk), and scores nobody needs are simply
   // not used, which keeps a single code path (and register allocation) for the
-  // loop.  The copy of a future K/V tile is issued from inside the pipeline.
-  auto mfma_phase = [&](int tslot, int kslot, int copy_tile, int copy_slot) __attribute__((always_inline)) {
-    // One base register per operand; every fragment address is that base plus
-    // an immediate offset.
-    const uint32_t tbase = opaque_vgpr((uint32_t)(size_t)(sVt + tslot * kTile) + taddr0);
+  // loop.
+  auto mfma_phase = [&](int tslot, int kslot, int copy_tile, int copy_slot, bool prefetched)
+                        __attribute__((always_inline)) {
+    const uint32_t tbase = tslot_base(tslot);
     const uint32_t kbase = opaque_vgpr((uint32_t)(size_t)(sK + kslot * kTile) + kaddr0);
-    auto load = [&](int i) __attribute__((always_inline)) {
-      uint32_t ad;
-      if (i < kNpv) ad = tbase + (uint32_t)((((i % DB) * 2 * (kBc / 8)) + 2 * (i / DB)) << 8);
-      else ad = kbase + (uint32_t)(((((i - kNpv) & 1) * 2 * CPR) + 2 * ((i - kNpv) >> 1)) << 8);
-      return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(size_t)ad);
-    };
     // The wave running products is preferred at instruction issue so that
     // its MFMAs are not held back by the other wave's softmax on the SIMD.
     __builtin_amdgcn_s_setprio(2);
-    V8 fr[kPipe];
+    if (!prefetched) {
 #pragma unroll
-    for (int i = 0; i < kPipe; ++i) fr[i] = load(i);
+      for (int i = 0; i < kPipe; ++i) fr[i] = load_op(tbase, kbase, i);
+    }
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int i = 0; i < kNpv + kNs; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       if (i < kNpv) {
-        const int c = i / DB;
+        const int c = pv_c(i);
         const u32x4 bw = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1], pk[c >> 1][4 * (c & 1) + 2],
                           pk[c >> 1][4 * (c & 1) + 3]};
         o[i % DB] = E::mfma(fr[i % kPipe], __builtin_bit_cast(V8, bw), o[i % DB]);
@@ -246,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
         const int k = i - kNpv;
         s[k & 1] = E::mfma(fr[i % kPipe], qf[k >> 1], s[k & 1]);
       }
-      if (i + kPipe < kNpv + kNs) fr[i % kPipe] = load(i + kPipe);
+      if (i + kPipe < kNpv + kNs) fr[i % kPipe] = load_op(tbase, kbase, i + kPipe);
       if (i == 6 && copy_tile >= 0) {
         __builtin_amdgcn_sched_barrier(0);
         issue_tile(copy_tile, copy_slot);
@@ -260,6 +279,35 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 8; ++r) pk[kb][r] = 0u;
+  };
+
+  // Half of V tile j (this group's share), staging -> V^T.  Wave w handles keys
+  // 8w .. 8w+7 (group 0 the first 32 keys, group 1 the rest).  For each span of
+  // 64 columns, two ds_read_b64_tr_b16 give lane (g, L) keys 8w + 0..3 and
+  // 8w + 4..7 of column 16g + L, which one ds_write_b128 stores as a whole
+  // 16-byte slot (each 16 lanes write 256 contiguous bytes).
+  const int tg = lane >> 4;
+  const int tl = lane & 15;
+  const int tch = 2 * tg + ((tl & 3) >> 1);  // source chunk within a span
+  const uint32_t trd0 = vs_byte<CPR>(8 * wave + (tl >> 2), tch) + 8 * (tl & 1);
+  const uint32_t trd1 = vs_byte<CPR>(8 * wave + 4 + (tl >> 2), tch) + 8 * (tl & 1);
+  const uint32_t twr0 = k_byte<kBc / 8>(16 * tg + tl, wave);
+  u32x2 tv[D / 64][2];  // transposed V data between its read and its write
+  auto transpose_read = [&](int j) __attribute__((always_inline)) {
+    const uint32_t src = (uint32_t)(size_t)(sVs + (j % kVSlots) * kTile);
+    const uint32_t a0 = opaque_vgpr(src + trd0), a1 = opaque_vgpr(src + trd1);
+#pragma unroll
+    for (int dq = 0; dq < D / 64; ++dq) {
+      const uint32_t so = (uint32_t)(dq * 8 * 256);  // chunk + 8 per span
+      tv[dq][0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(a0 + so)));
+      tv[dq][1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(a1 + so)));
+    }
+  };
+  auto transpose_write = [&](int j) __attribute__((always_inline)) {
+    const uint32_t dst = opaque_vgpr((uint32_t)(size_t)(sVt + (j % kTSlots) * kTile) + twr0);
+#pragma unroll
+    for (int dq = 0; dq < D / 64; ++dq)
+      *(FA2_LDS u32x4*)(size_t)(dst + (uint32_t)(dq * 32 * 256)) = u32x4{tv[dq][0][0], tv[dq][0][1], tv[dq][1][0], tv[dq][1][1]};
   };
 
   // Softmax of tile j into pk, updating the row statistics.  The reference max
@@ -349,35 +397,6 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
     l_part += lsum;
   };
 
-  // Half of V tile j (this group's share), staging -> V^T.  Wave w handles keys
-  // 8w .. 8w+7 (group 0 the first 32 keys, group 1 the rest).  For each span of
-  // 64 columns, two ds_read_b64_tr_b16 give lane (g, L) keys 8w + 0..3 and
-  // 8w + 4..7 of column 16g + L, which one ds_write_b128 stores as a whole
-  // 16-byte slot (each 16 lanes write 256 contiguous bytes).
-  const int tg = lane >> 4;
-  const int tl = lane & 15;
-  const int tch = 2 * tg + ((tl & 3) >> 1);  // source chunk within a span
-  const uint32_t trd0 = vs_byte<CPR>(8 * wave + (tl >> 2), tch) + 8 * (tl & 1);
-  const uint32_t trd1 = vs_byte<CPR>(8 * wave + 4 + (tl >> 2), tch) + 8 * (tl & 1);
-  const uint32_t twr0 = k_byte<kBc / 8>(16 * tg + tl, wave);
-  u32x2 tv[D / 64][2];  // transposed V data between its read and its write
-  auto transpose_read = [&](int j) __attribute__((always_inline)) {
-    const uint32_t src = (uint32_t)(size_t)(sVs + (j % kVSlots) * kTile);
-    const uint32_t a0 = opaque_vgpr(src + trd0), a1 = opaque_vgpr(src + trd1);
-#pragma unroll
-    for (int dq = 0; dq < D / 64; ++dq) {
-      const uint32_t so = (uint32_t)(dq * 8 * 256);  // chunk + 8 per span
-      tv[dq][0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(a0 + so)));
-      tv[dq][1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(a1 + so)));
-    }
-  };
-  auto transpose_write = [&](int j) __attribute__((always_inline)) {
-    const uint32_t dst = opaque_vgpr((uint32_t)(size_t)(sVt + (j % kTSlots) * kTile) + twr0);
-#pragma unroll
-    for (int dq = 0; dq < D / 64; ++dq)
-      *(FA2_LDS u32x4*)(size_t)(dst + (uint32_t)(dq * 32 * 256)) = u32x4{tv[dq][0][0], tv[dq][0][1], tv[dq][1][0], tv[dq][1][1]};
-  };
-
   // Step st: both groups meet at the two barriers; in between, group 0 runs
   // [P.V(st-1), S(st)] then [softmax(st), transpose half of V(st)], and group 1
   // runs [softmax(st-1), transpose half of V(st)] then [P.V(st-1), S(st)].
@@ -400,14 +419,21 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       wait_vm_lds_barrier<2 * kLoads>();
       __builtin_amdgcn_sched_barrier(0);
-      mfma_phase((st + kTSlots - 1) % kTSlots, st % kKSlots, copy_tile_of(st), (st + 2) % kKSlots);
+      // The zeroed V^T slot read at st = 0 is visible only after this barrier.
+      mfma_phase((st + kTSlots - 1) % kTSlots, st % kKSlots, copy_tile_of(st), (st + 2) % kKSlots, st > 0);
       __builtin_amdgcn_sched_barrier(0);
       lds_done_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (st < nt) transpose_read(st);
-      if (st < nt && wave_active(st)) softmax(st);
-      else zero_pk();
-      if (st < nt) transpose_write(st);
+      if (st < nt) {
+        transpose_read(st);
+        if (wave_active(st)) softmax(st);
+        else zero_pk();
+        transpose_write(st);
+        __builtin_amdgcn_sched_barrier(0);
+        prefetch(st % kTSlots);  // keys 32-63 of V^T(st), written by group 1
+      } else {
+        zero_pk();
+      }
     }
   } else {
     for (int st = 0; st <= nt; ++st) {
@@ -419,9 +445,11 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
       else zero_pk();
       if (st < nt) transpose_write(st);
       __builtin_amdgcn_sched_barrier(0);
+      prefetch((st + kTSlots - 1) % kTSlots);  // V^T(st-1): complete since the step's first barrier
+      __builtin_amdgcn_sched_barrier(0);
       lds_done_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      mfma_phase((st + kTSlots - 1) % kTSlots, st % kKSlots, copy_tile_of(st), (st + 2) % kKSlots);
+      mfma_phase((st + kTSlots - 1) % kTSlots, st % kKSlots, copy_tile_of(st), (st + 2) % kKSlots, true);
     }
   }
   // No LDS write may still be in flight when the workgroup retires.

@@ -158,6 +158,15 @@ def test_parity_reference_moves(dtype, d, pattern):
         _compare(o, lse, o_ref, l_ref, dtype, f"{pattern} causal={causal}")
 
 
+@pytest.mark.parametrize("B,H,N,d", [(1, 24, 4000, 64), (2, 8, 600, 128), (1, 16, 2500, 128)])
+def test_parity_causal_head_groups(B, H, N, d):
+    """Causal launches whose head count is a multiple of 8 order their query
+    tiles in groups of heads per XCD, a smaller last group included (24 heads
+    of 16 query tiles: each XCD takes 3 heads, as a group of 2 and then 1);
+    every (batch, head, query tile) must still be computed exactly once."""
+    _full_parity(B, H, N, d, torch.float16, True, seed=5)
+
+
 # --- named workloads at full size ------------------------------------------------------
 
 def _sample_rows(N, rng, n_random=40):

@@ -11,6 +11,10 @@ Contents
     natural-log logsumexp per row) in fp64, implemented in ``attention_ref.c``
     and loaded through ctypes.  See that file's header for the passages of the
     pages it follows.
+``attention_bwd_f64``
+    The gradients dQ, dK, dV of that definition for a given dO (and the row
+    statistic D), by the chain rule in fp64, implemented in
+    ``attention_bwd_ref.c``.
 ``tiled``
     A numpy model of the tiled forward recurrence the pages describe (online
     softmax, delayed normalisation, block-level causal skip).  It is used only to
@@ -30,15 +34,17 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attention_ref.c")
+_BWD_SRC = os.path.join(_HERE, "attention_bwd_ref.c")
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 _lib_cache: dict[str, ctypes.CDLL] = {}
 
 
-def build(src: str = _SRC, out: str = LIB_PATH) -> str:
-    """Compile the C oracle with gcc (no fast-math: IEEE fp64 throughout)."""
+def build(src: str = _SRC, out: str = LIB_PATH, bwd_src: str = _BWD_SRC) -> str:
+    """Compile the C oracle (forward and gradient sources) with gcc (no
+    fast-math: IEEE fp64 throughout)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-           "-ffp-contract=off", "-pthread", src, "-o", out, "-lm"]
+           "-ffp-contract=off", "-pthread", src, bwd_src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -61,6 +67,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oracle_attention_rows_f64.argtypes = [dp, dp, dp, lp, i64, dp, dp, i64, i64,
                                               ctypes.c_int, ctypes.c_double, ctypes.c_int]
     lib.oracle_attention_rows_f64.restype = ctypes.c_int
+    lib.oracle_attention_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                             ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.oracle_attention_bwd_f64.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
 
@@ -138,3 +147,33 @@ def attention_rows_f64(q, k, v, rows, causal: bool, scale: float, nthreads: int 
         raise RuntimeError(f"oracle_attention_rows_f64 failed with code {rc}")
     return o, lse
 
+
+
+def attention_bwd_f64(q, k, v, dout, causal: bool, scale: float, nthreads: int | None = None,
+                      lib_path: str = LIB_PATH):
+    """Gradients of exact attention over [B, H, N, d] (or [N, d]) fp64 arrays.
+
+    ``dout`` is the gradient with respect to the output O.  Returns
+    ``(dq, dk, dv, delta)``: three arrays shaped like ``q`` and the row
+    statistic D = rowsum(P o dP), shaped like ``q.shape[:-1]``.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    if not (q.shape == k.shape == v.shape == dout.shape):
+        raise ValueError(f"shape mismatch {q.shape} {k.shape} {v.shape} {dout.shape}")
+    squeeze = q.ndim == 2
+    if squeeze:
+        q, k, v, dout = q[None, None], k[None, None], v[None, None], dout[None, None]
+    if q.ndim != 4:
+        raise ValueError("expected [B, H, N, d] or [N, d]")
+    B, H, N, d = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    delta = np.empty((B, H, N), dtype=np.float64)
+    lib = load(lib_path)
+    rc = lib.oracle_attention_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(delta), B, H, N, d, int(bool(causal)), float(scale),
+                                      _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_bwd_f64 failed with code {rc}")
+    if squeeze:
+        return dq[0, 0], dk[0, 0], dv[0, 0], delta[0, 0]
+    return dq, dk, dv, delta

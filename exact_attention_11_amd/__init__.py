@@ -1,14 +1,17 @@
-"""Fused exact-attention forward pass for AMD Instinct MI355X (gfx950).
+"""Fused exact attention for AMD Instinct MI355X (gfx950): forward pass and
+gradients.
 
 Thin Python binding of the C ABI declared in ``include/fa2.h``; every step of
 the computation runs in the HIP kernels of ``libfa2.so``.  torch supplies device
 memory and streams only.
 
     o, lse = exact_attention_11_amd.forward(q, k, v, causal=True)
+    dq, dk, dv = exact_attention_11_amd.backward(q, k, v, o, do, lse, causal=True)
 
 ``q, k, v``: [B, H, N, d] fp16 or bf16 CUDA (HIP) tensors, contiguous.
-Returns ``o`` (same shape and dtype) and ``lse`` ([B, H, N] float32, the
-natural-log logsumexp of each row's scaled, masked scores).
+``forward`` returns ``o`` (same shape and dtype) and ``lse`` ([B, H, N] float32,
+the natural-log logsumexp of each row's scaled, masked scores); ``backward``
+takes those and the gradient ``do`` of a loss with respect to ``o``.
 """
 from __future__ import annotations
 
@@ -34,14 +37,14 @@ FA2_ERR_DEVICE = 8
 FA2_ERR_LAUNCH = 9
 
 # Every symbol include/fa2.h declares.
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_status_str", "fa2_last_hip_error")
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_bwd", "fa2_status_str", "fa2_last_hip_error")
 
 HEAD_DIMS = (64, 128, 256)
 
 
 class Fa2Error(RuntimeError):
-    def __init__(self, status: int, msg: str):
-        super().__init__(f"fa2_fwd failed: {msg} (status {status})")
+    def __init__(self, status: int, msg: str, entry: str = "fa2_fwd"):
+        super().__init__(f"{entry} failed: {msg} (status {status})")
         self.status = status
 
 
@@ -66,6 +69,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                             ctypes.c_int, vp]
     lib.fa2_fwd.restype = ctypes.c_int
+    lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                            ctypes.c_float, ctypes.c_int, vp]
+    lib.fa2_bwd.restype = ctypes.c_int
     lib.fa2_status_str.argtypes = [ctypes.c_int]
     lib.fa2_status_str.restype = ctypes.c_char_p
     lib.fa2_last_hip_error.argtypes = []
@@ -80,6 +86,13 @@ def fa2_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d:
     """Direct call of the C entry point with raw device addresses; returns the status."""
     return load_library().fa2_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), int(dtype),
                                   stream)
+
+
+def fa2_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, delta: int, dq: int, dk: int, dv: int,
+            B: int, H: int, N: int, d: int, causal: int, scale: float, dtype: int, stream: int) -> int:
+    """Direct call of the gradient entry point with raw device addresses; returns the status."""
+    return load_library().fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, int(causal),
+                                  float(scale), int(dtype), stream)
 
 
 def fa2_status_str(status: int) -> str:
@@ -137,3 +150,48 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if rc != FA2_OK:
         raise Fa2Error(rc, fa2_status_str(rc))
     return out, lse
+
+
+def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, stream=None,
+             delta=None, dq=None, dk=None, dv=None):
+    """Gradients of attention on the GPU.  Returns ``(dq, dk, dv)``.
+
+    ``o`` and ``lse`` are the forward pass's outputs for the same ``q, k, v``,
+    ``causal`` and ``scale``; ``dout`` is the gradient of the loss with respect
+    to ``o``.  ``delta`` ([B, H, N] float32) receives the row statistic
+    D = rowsum(dout * o); it and the outputs are allocated here unless given.
+    """
+    import torch
+
+    ts = (q, k, v, o, dout)
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("q, k, v, o, dout must share one [B, H, N, d] shape")
+    if any(t.dtype != q.dtype for t in ts):
+        raise TypeError("q, k, v, o, dout must share one dtype")
+    code = _dtype_code(q)
+    if any(not t.is_cuda or t.device != q.device for t in ts + (lse,)):
+        raise ValueError("all tensors must be on one GPU")
+    if any(not t.is_contiguous() for t in ts + (lse,)):
+        raise ValueError("all tensors must be contiguous")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t in (dq, dk, dv):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("dq, dk, dv must be contiguous tensors like q")
+    if delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 [B, H, N] tensor")
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                     delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                     int(bool(causal)), float(scale), code, s.cuda_stream)
+    if rc != FA2_OK:
+        raise Fa2Error(rc, fa2_status_str(rc), "fa2_bwd")
+    return dq, dk, dv

@@ -1,5 +1,6 @@
-// fa2_api.hip -- C ABI of the fused attention forward pass (declared in
-// include/fa2.h): argument checks, device check, instance dispatch and launch.
+// fa2_api.hip -- C ABI of the fused attention forward pass and of its
+// gradients (declared in include/fa2.h): argument checks, device check,
+// instance dispatch and launch.
 //
 // Instances: element type {fp16, bf16} x head dim {64, 128, 256} x {no mask,
 // causal}.  The head-dim limit of 256 follows "FlashAttention-2: Where the Second
@@ -11,6 +12,7 @@
 #include <cstring>
 
 #include "fa2.h"
+#include "fa2_bwd.h"
 #include "fa2_fwd_4wave.h"
 #include "fa2_fwd_8wave.h"
 
@@ -78,6 +80,34 @@ hipError_t launch_d(const fa2::FwdArgs& args, int64_t d, bool causal, hipStream_
   }
 }
 
+template <int kDType, int D, bool kCausal>
+hipError_t launch_bwd(const fa2::bwd::BwdArgs& args, hipStream_t stream) {
+  using namespace fa2::bwd;
+  const int64_t rows = (int64_t)args.BH * args.N;
+  hipLaunchKernelGGL((fa2_bwd_delta<kDType, D>), dim3((unsigned)((rows + kDeltaRows - 1) / kDeltaRows)), dim3(256),
+                     0, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa2_bwd_dkdv<kDType, D, kCausal>), dim3((unsigned)(args.n_kv_wg * args.BH)), dim3(kThreads), 0,
+                     stream, args);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa2_bwd_dq<kDType, D, kCausal>), dim3((unsigned)(args.n_q_wg * args.BH)), dim3(kThreads), 0,
+                     stream, args);
+  return hipGetLastError();
+}
+
+template <int kDType>
+hipError_t launch_bwd_d(const fa2::bwd::BwdArgs& args, int64_t d, bool causal, hipStream_t stream) {
+  switch (d) {
+    case 64: return causal ? launch_bwd<kDType, 64, true>(args, stream) : launch_bwd<kDType, 64, false>(args, stream);
+    case 128:
+      return causal ? launch_bwd<kDType, 128, true>(args, stream) : launch_bwd<kDType, 128, false>(args, stream);
+    default:
+      return causal ? launch_bwd<kDType, 256, true>(args, stream) : launch_bwd<kDType, 256, false>(args, stream);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -91,7 +121,7 @@ const char* fa2_status_str(int status) {
     case FA2_ERR_DTYPE: return "dtype must be FA2_DTYPE_FP16 or FA2_DTYPE_BF16";
     case FA2_ERR_SCALE: return "scale must be finite";
     case FA2_ERR_ALIGN: return "pointers must be 16-byte aligned";
-    case FA2_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA2_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA2_ERR_DEVICE: return "no usable gfx950 device";
     case FA2_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
@@ -146,6 +176,74 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_d<0>(args, d, causal != 0, s) : launch_d<1>(args, d, causal != 0, s);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA2_ERR_LAUNCH;
+  }
+  return FA2_OK;
+}
+
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+            float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+            float scale, int dtype, void* stream) {
+  g_last_hip_error = 0;
+  // ---- argument checks: no HIP call before they all pass -------------------
+  if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA2_ERR_HEADDIM;
+  if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
+  const float c2 = (float)((double)scale * 1.4426950408889634074);
+  if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) return FA2_OK;
+  if (N > (int64_t)INT32_MAX - 256) return FA2_ERR_SHAPE;
+  if (B > INT32_MAX || H > INT32_MAX) return FA2_ERR_SHAPE;
+  const int64_t bh = B * H;
+  const int64_t n_kv = (N + fa2::bwd::kKeysPerWg - 1) / fa2::bwd::kKeysPerWg;
+  const int64_t n_q = (N + fa2::bwd::kRowsPerWg - 1) / fa2::bwd::kRowsPerWg;
+  if (bh > (int64_t)INT32_MAX / (n_kv > n_q ? n_kv : n_q)) return FA2_ERR_SHAPE;
+  if (bh > (INT64_MAX / 4) / (N * d)) return FA2_ERR_SHAPE;
+  if ((bh * N + fa2::bwd::kDeltaRows - 1) / fa2::bwd::kDeltaRows > (int64_t)INT32_MAX) return FA2_ERR_SHAPE;
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FA2_ERR_NULLPTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)lse |
+       (uintptr_t)delta | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15)
+    return FA2_ERR_ALIGN;
+  const uint64_t tb = (uint64_t)(bh * N * d) * 2;
+  const uint64_t sb = (uint64_t)(bh * N) * 4;
+  const void* in[6] = {q, k, v, o, dout, lse};
+  const uint64_t in_n[6] = {tb, tb, tb, tb, tb, sb};
+  const void* out[4] = {delta, dq, dk, dv};
+  const uint64_t out_n[4] = {sb, tb, tb, tb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i], out_n[i], in[j], in_n[j])) return FA2_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out_n[i], out[j], out_n[j])) return FA2_ERR_ALIAS;
+  }
+
+  // ---- device ---------------------------------------------------------------
+  const int dev_status = check_device();
+  if (dev_status != FA2_OK) return dev_status;
+
+  fa2::bwd::BwdArgs args;
+  args.q = (const uint16_t*)q;
+  args.k = (const uint16_t*)k;
+  args.v = (const uint16_t*)v;
+  args.o = (const uint16_t*)o;
+  args.dout = (const uint16_t*)dout;
+  args.lse = lse;
+  args.delta = delta;
+  args.dq = (uint16_t*)dq;
+  args.dk = (uint16_t*)dk;
+  args.dv = (uint16_t*)dv;
+  args.N = (int)N;
+  args.BH = (int)bh;
+  args.n_kv_wg = (int)n_kv;
+  args.n_q_wg = (int)n_q;
+  args.scale = scale;
+  args.c2 = c2;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_bwd_d<0>(args, d, causal != 0, s)
+                                         : launch_bwd_d<1>(args, d, causal != 0, s);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FA2_ERR_LAUNCH;

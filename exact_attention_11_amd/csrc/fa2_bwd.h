@@ -1,0 +1,474 @@
+// fa2_bwd.h -- gradients of exact attention for gfx950 (head dims 64, 128, 256).
+//
+// What the pages fix, and where it lives here:
+//  * The backward pass recomputes the probabilities from the saved row
+//    statistic instead of storing them: P = exp(s - L) with L the forward's
+//    logsumexp ("6.2 FlashAttention V2 in depth", section 7.1; "Flash
+//    Attention: Memory-Efficient Attention at Scale", section "Recomputation
+//    in the backward pass").
+//  * The softmax gradient is dS = P o (dP - D) with D = rowsum(dO o O), and D
+//    is computed once for all rows by a separate preprocess kernel before the
+//    main loop ("6.2 FlashAttention V2 in depth", section 7.3): fa2_bwd_delta.
+//  * The main backward loop runs over key/value tiles outside and query tiles
+//    inside, so the dK and dV of a key tile are accumulated by one workgroup
+//    alone; dQ must then be gathered across workgroups, either by atomic adds
+//    or by a second pass (same page, section 7.2).  This file takes the second
+//    pass: fa2_bwd_dkdv (key tiles outside) writes dK and dV, fa2_bwd_dq (query
+//    tiles outside, as in the forward pass) writes dQ.  Both recompute the
+//    scores; no atomics, no fp32 dQ buffer, and the result is bitwise
+//    reproducible.
+//  * The gradients themselves follow from s = scale * q.k, p = softmax(s),
+//    o = p.v by the chain rule: dV = P^T dO, dP = dO V^T, dQ = scale dS K,
+//    dK = scale dS^T Q.
+//
+// gfx950 mapping.  Four wavefronts per workgroup (one per SIMD: the dK and dV
+// accumulators of 32 keys take 128 registers at d = 128, 256 at d = 256).
+// All products run on v_mfma_f32_32x32x16 with fp32 accumulation.
+//  * fa2_bwd_dkdv: wave w owns keys kw0 .. kw0+31 and keeps K and V of those
+//    keys in registers as the B operands of S = Q K^T and dP = dO V^T; the Q and
+//    dO tiles (64 rows) stream through LDS.  In the accumulator of S a lane
+//    holds one key and 16 queries, so P and dS feed dV^T += dO^T P and
+//    dK^T += Q^T dS directly as B operands; the A operands (dO^T, Q^T) come
+//    from the same LDS tiles through ds_read_b64_tr_b16, reading the query rows
+//    in the order the accumulator holds them.
+//  * fa2_bwd_dq: the forward's layout: S^T = K Q^T and dP^T = V dO^T with Q and
+//    dO of the wave's 32 rows in registers and K, V tiles in LDS; a lane holds
+//    one query, so L and D are per-lane scalars; dQ^T += K^T dS^T reads K^T
+//    through ds_read_b64_tr_b16.
+//  * Every LDS tile is row-major with the 16-byte chunk index XORed by a
+//    rotation of the low row bits, which keeps both the row reads (MFMA A
+//    operands) and the transposed reads free of bank conflicts.
+#pragma once
+
+#include "fa2_common.h"
+
+namespace fa2 {
+namespace bwd {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKeysPerWg = 32 * kWaves;  // fa2_bwd_dkdv: keys per workgroup
+constexpr int kQTile = 64;               // fa2_bwd_dkdv: query rows per streamed tile
+constexpr int kRowsPerWg = 32 * kWaves;  // fa2_bwd_dq: query rows per workgroup
+constexpr int kKTile = 64;               // fa2_bwd_dq: keys per streamed tile
+constexpr int kDeltaRows = 16;           // fa2_bwd_delta: rows per workgroup (16 lanes each)
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;  // [B, H, N] natural-log logsumexp from the forward pass
+  float* delta;      // [B, H, N] D = rowsum(dO o O), written by fa2_bwd_delta
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int N;
+  int BH;
+  int n_kv_wg;  // ceil(N / kKeysPerWg)
+  int n_q_wg;   // ceil(N / kRowsPerWg)
+  float scale;  // multiplier of the scores
+  float c2;     // scale * log2(e)
+};
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Chunk swizzle of the LDS tiles: chunk c of row r is stored at c ^ swz(r).
+// Over any 16 consecutive rows swz takes 16 distinct values in the low 4 bits
+// (row reads of 16 lanes hit 16 distinct 16-byte bank groups), and the 4 rows
+// of a transposed read (aligned to 4) get XOR values 4 apart, so chunks c and
+// c + 1 of those rows land on 8 distinct bank groups.  At d = 64 two rows share
+// a 256-byte bank window and the rotation runs on row / 2.
+template <int D> __device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 64) {
+    const int x = (row >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+  } else {
+    const int x = row & 15;
+    return ((x & 3) << 2) | (x >> 2);
+  }
+}
+template <int D> __device__ __forceinline__ uint32_t tile_byte(int row, int chunk) {
+  return (uint32_t)(row * D * 2 + ((chunk ^ swz<D>(row)) << 4));
+}
+
+// Copy R rows (r0.., clamped to N - 1) of a [N, D] head into an LDS tile; each
+// instruction of a wave fills 64 consecutive 16-byte slots.
+template <int D, int R>
+__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2_LDS uint16_t* dst, int r0, int N,
+                                          int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int kPer = R * CPR / (64 * kWaves);
+  static_assert(kPer * 64 * kWaves == R * CPR, "tile copy split");
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const int s0 = (t * kWaves + wave) * 64;
+    const int s = s0 + lane;
+    const int row = s / CPR;
+    const int ch = (s % CPR) ^ swz<D>(row);
+    const int grow = min(r0 + row, N - 1);
+    dma16(head + (int64_t)grow * D + ch * 8, dst + s0 * 8);
+  }
+}
+
+// One global_load_lds_dword: every lane copies 4 bytes to lds_base + 4 * lane.
+__device__ __forceinline__ void dma4(const void* g, FA2_LDS void* lds_base) {
+  const uint32_t m0v = (uint32_t)(size_t)lds_base;
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
+}
+
+template <int kDType> __device__ __forceinline__ float to_f32(uint16_t x) {
+  if constexpr (kDType == 0) return (float)__builtin_bit_cast(_Float16, x);
+  else return __uint_as_float((uint32_t)x << 16);
+}
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO o O) for every row of every head, in fp32.  16 lanes per row.
+template <int kDType, int D>
+__global__ __launch_bounds__(256) void fa2_bwd_delta(BwdArgs a) {
+  constexpr int kPer = D / 16;  // elements per lane: 4, 8 or 16
+  const int t = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * kDeltaRows + (t >> 4);
+  const int part = t & 15;
+  const int64_t rows = (int64_t)a.BH * a.N;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint16_t* op = a.o + row * D + part * kPer;
+    const uint16_t* gp = a.dout + row * D + part * kPer;
+#pragma unroll
+    for (int c = 0; c < kPer; c += 4) {
+      const u32x2 ov = *(const u32x2*)(op + c);
+      const u32x2 gv = *(const u32x2*)(gp + c);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc += to_f32<kDType>((uint16_t)(ov[h] & 0xffffu)) * to_f32<kDType>((uint16_t)(gv[h] & 0xffffu));
+        acc += to_f32<kDType>((uint16_t)(ov[h] >> 16)) * to_f32<kDType>((uint16_t)(gv[h] >> 16));
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (part == 0 && row < rows) a.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV of kKeysPerWg keys of one head; query tiles stream through LDS.
+template <int kDType, int D, bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv(BwdArgs a) {
+  typedef Elem<kDType> E;
+  typedef typename E::V8 V8;
+  constexpr int KS = D / 16;  // k-steps of S = Q K^T over the head dim
+  constexpr int DB = D / 32;  // 32-wide blocks of the head dim
+  constexpr int kTile = kQTile * D;
+
+  // [buffer][Q | dO] tiles, then [buffer][L | D] rows (64 floats each).
+  __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];
+  __shared__ __attribute__((aligned(1024))) float stat_[2][2][kQTile];
+  FA2_LDS uint16_t* const sT = (FA2_LDS uint16_t*)smem_;
+  FA2_LDS float* const sS = (FA2_LDS float*)&stat_[0][0][0];
+
+  const int N = a.N;
+  // Key tiles with a low index see the most query tiles under the causal mask:
+  // dispatch all heads' first key tiles first.
+  const int kt = blockIdx.x / a.BH;
+  const int bh = blockIdx.x - kt * a.BH;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int col = lane & 31;
+  const int kw0 = kt * kKeysPerWg + wave * 32;  // this wave's first key
+  const int my_k = kw0 + col;                   // the key of this lane's accumulator column
+  const int64_t head_off = (int64_t)bh * N * D;
+  const uint16_t* __restrict__ qh = a.q + head_off;
+  const uint16_t* __restrict__ gh = a.dout + head_off;
+  const float* __restrict__ lh = a.lse + (int64_t)bh * N;
+  const float* __restrict__ dh = a.delta + (int64_t)bh * N;
+
+  const int it0 = kCausal ? (kt * kKeysPerWg) / kQTile : 0;  // first query tile that sees these keys
+  const int it1 = (N + kQTile - 1) / kQTile;
+
+  auto load_tile = [&](int it, int buf) __attribute__((always_inline)) {
+    load_rows<D, kQTile>(qh, sT + (2 * buf + 0) * kTile, it * kQTile, N, wave, lane);
+    load_rows<D, kQTile>(gh, sT + (2 * buf + 1) * kTile, it * kQTile, N, wave, lane);
+    if (wave == 0) {
+      const int r = min(it * kQTile + lane, N - 1);
+      dma4(lh + r, sS + (2 * buf + 0) * kQTile);
+      dma4(dh + r, sS + (2 * buf + 1) * kQTile);
+    }
+  };
+  load_tile(it0, 0);
+
+  // K and V of this lane's key (B operands of S = Q K^T and dP = dO V^T).
+  V8 kf[KS], vf[KS];
+  {
+    const int r = min(my_k, N - 1);
+    const uint16_t* kp = a.k + head_off + (int64_t)r * D + 8 * hl;
+    const uint16_t* vp = a.v + head_off + (int64_t)r * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(kp + 16 * ks));
+      vf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(vp + 16 * ks));
+    }
+  }
+
+  f32x16 dkt[DB], dvt[DB];  // dK^T, dV^T: rows = head dim, columns = this wave's keys
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dkt[db] = f32x16{};
+    dvt[db] = f32x16{};
+  }
+
+  // Transposed-read addresses (rows = queries of a 16-query k-step, in the
+  // order the S accumulator holds them; columns = 4 head dims).
+  const int tg = lane >> 4;
+  const int tl = lane & 15;
+
+  for (int it = it0; it < it1; ++it) {
+    const int buf = (it - it0) & 1;
+    // Tile it has landed for every wave; every wave is done with the other buffer.
+    wait_vm_lds_barrier<0>();
+    if (it + 1 < it1) load_tile(it + 1, buf ^ 1);
+    const FA2_LDS uint16_t* tq = sT + (2 * buf + 0) * kTile;
+    const FA2_LDS uint16_t* tg_ = sT + (2 * buf + 1) * kTile;
+    const FA2_LDS float* tL = sS + (2 * buf + 0) * kQTile;
+    const FA2_LDS float* tD = sS + (2 * buf + 1) * kQTile;
+#pragma unroll
+    for (int sb = 0; sb < kQTile / 32; ++sb) {
+      const int q0 = it * kQTile + sb * 32;
+      if (q0 >= N) break;
+      if (kCausal && q0 + 31 < kw0) continue;  // every query precedes every key of this wave
+      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t off = tile_byte<D>(sb * 32 + col, 2 * ks + hl);
+        const V8 aq = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)((const FA2_LDS char*)tq + off));
+        const V8 ag = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)((const FA2_LDS char*)tg_ + off));
+        s = E::mfma(aq, kf[ks], s);
+        dp = E::mfma(ag, vf[ks], dp);
+      }
+      // Element e of the accumulators is query q0 + 8*(e/4) + 4*hl + e%4 of this
+      // lane's key; its L and D sit at the same offset in the stat rows.
+      const bool need_mask = (q0 + 32 > N) || (kCausal && kw0 + 31 > q0);
+      const int lim_n = N - q0 - 4 * hl;          // query < N      <=> qi < lim_n
+      const int lim_c = my_k - q0 - 4 * hl;       // key <= query   <=> qi >= lim_c
+      uint32_t pp[2][4], pd[2][4];                // P and dS packed, per 16-query k-step
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 lw = *(const FA2_LDS u32x4*)(tL + sb * 32 + 8 * g + 4 * hl);
+        const u32x4 dw = *(const FA2_LDS u32x4*)(tD + sb * 32 + 8 * g + 4 * hl);
+        float p[4], ds[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * g + i;
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c2, -__uint_as_float(lw[i]) * kLog2e));
+          if (need_mask) {
+            const int qi = 8 * g + i;
+            const bool ok = qi < lim_n && (!kCausal || qi >= lim_c);
+            x = ok ? x : 0.f;
+          }
+          p[i] = x;
+          ds[i] = x * (dp[e] - __uint_as_float(dw[i]));
+        }
+        pp[g >> 1][2 * (g & 1) + 0] = E::pack2(p[0], p[1]);
+        pp[g >> 1][2 * (g & 1) + 1] = E::pack2(p[2], p[3]);
+        pd[g >> 1][2 * (g & 1) + 0] = E::pack2(ds[0], ds[1]);
+        pd[g >> 1][2 * (g & 1) + 1] = E::pack2(ds[2], ds[3]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps.
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const V8 bp = __builtin_bit_cast(V8, u32x4{pp[c][0], pp[c][1], pp[c][2], pp[c][3]});
+        const V8 bd = __builtin_bit_cast(V8, u32x4{pd[c][0], pd[c][1], pd[c][2], pd[c][3]});
+        const int r1 = sb * 32 + 16 * c + 4 * (tg >> 1) + (tl >> 2);
+        const int r2 = r1 + 8;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int dim = 32 * db + 16 * (tg & 1) + 4 * (tl & 3);
+          const uint32_t o1 = tile_byte<D>(r1, dim >> 3) + 8 * ((dim >> 2) & 1);
+          const uint32_t o2 = tile_byte<D>(r2, dim >> 3) + 8 * ((dim >> 2) & 1);
+          const u32x2 g1 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tg_ + o1)));
+          const u32x2 g2 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tg_ + o2)));
+          const u32x2 q1 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tq + o1)));
+          const u32x2 q2 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tq + o2)));
+          dvt[db] = E::mfma(__builtin_bit_cast(V8, u32x4{g1[0], g1[1], g2[0], g2[1]}), bp, dvt[db]);
+          dkt[db] = E::mfma(__builtin_bit_cast(V8, u32x4{q1[0], q1[1], q2[0], q2[1]}), bd, dkt[db]);
+        }
+      }
+    }
+  }
+  // No LDS write may still be in flight when the workgroup retires.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Element e of block db is head dim 32*db + 8*(e/4) + 4*hl + e%4 of key my_k.
+  if (my_k < N) {
+    uint16_t* kp = a.dk + head_off + (int64_t)my_k * D;
+    uint16_t* vp = a.dv + head_off + (int64_t)my_k * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = 32 * db + 8 * r4 + 4 * hl;
+        *(u32x2*)(kp + dim) = u32x2{E::pack2(dkt[db][4 * r4 + 0] * a.scale, dkt[db][4 * r4 + 1] * a.scale),
+                                    E::pack2(dkt[db][4 * r4 + 2] * a.scale, dkt[db][4 * r4 + 3] * a.scale)};
+        *(u32x2*)(vp + dim) = u32x2{E::pack2(dvt[db][4 * r4 + 0], dvt[db][4 * r4 + 1]),
+                                    E::pack2(dvt[db][4 * r4 + 2], dvt[db][4 * r4 + 3])};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ of kRowsPerWg query rows of one head; key/value tiles stream through LDS.
+template <int kDType, int D, bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dq(BwdArgs a) {
+  typedef Elem<kDType> E;
+  typedef typename E::V8 V8;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int kTile = kKTile * D;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];  // [buffer][K | V]
+  FA2_LDS uint16_t* const sT = (FA2_LDS uint16_t*)smem_;
+
+  const int N = a.N;
+  // Under the causal mask the last query tiles see the most keys: dispatch
+  // all heads' last tiles first.
+  const int level = blockIdx.x / a.BH;
+  const int bh = blockIdx.x - level * a.BH;
+  const int qt = kCausal ? a.n_q_wg - 1 - level : level;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int col = lane & 31;
+  const int q_row0 = qt * kRowsPerWg + wave * 32;
+  const int my_q = q_row0 + col;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const uint16_t* __restrict__ kh = a.k + head_off;
+  const uint16_t* __restrict__ vh = a.v + head_off;
+
+  const int kv_end = kCausal ? min(N, (qt + 1) * kRowsPerWg) : N;
+  const int nt = (kv_end + kKTile - 1) / kKTile;
+
+  auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
+    load_rows<D, kKTile>(kh, sT + (2 * buf + 0) * kTile, j * kKTile, N, wave, lane);
+    load_rows<D, kKTile>(vh, sT + (2 * buf + 1) * kTile, j * kKTile, N, wave, lane);
+  };
+  load_tile(0, 0);
+
+  // Q and dO of this lane's query row (B operands of S^T = K Q^T, dP^T = V dO^T),
+  // and its L (in log2 units) and D.
+  V8 qf[KS], gf[KS];
+  const int rq = min(my_q, N - 1);
+  {
+    const uint16_t* qp = a.q + head_off + (int64_t)rq * D + 8 * hl;
+    const uint16_t* gp = a.dout + head_off + (int64_t)rq * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(qp + 16 * ks));
+      gf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(gp + 16 * ks));
+    }
+  }
+  const float l2 = a.lse[(int64_t)bh * N + rq] * kLog2e;
+  const float dd = a.delta[(int64_t)bh * N + rq];
+
+  f32x16 dqt[DB];  // dQ^T: rows = head dim, columns = this wave's queries
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
+
+  const int tg = lane >> 4;
+  const int tl = lane & 15;
+
+  for (int j = 0; j < nt; ++j) {
+    const int buf = j & 1;
+    wait_vm_lds_barrier<0>();
+    if (j + 1 < nt) load_tile(j + 1, buf ^ 1);
+    const int kv0 = j * kKTile;
+    const bool active = !kCausal || kv0 <= q_row0 + 31;
+    if (!active) continue;  // wave-uniform; the barriers stay in step
+    const FA2_LDS uint16_t* tk = sT + (2 * buf + 0) * kTile;
+    const FA2_LDS uint16_t* tv = sT + (2 * buf + 1) * kTile;
+    // S^T = K Q^T and dP^T = V dO^T for 64 keys x this wave's 32 queries.
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t off = tile_byte<D>(32 * kb + col, 2 * ks + hl);
+        const V8 ak = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)((const FA2_LDS char*)tk + off));
+        const V8 av = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)((const FA2_LDS char*)tv + off));
+        s[kb] = E::mfma(ak, qf[ks], s[kb]);
+        dp[kb] = E::mfma(av, gf[ks], dp[kb]);
+      }
+    }
+    // Element (kb, e) is key kv0 + 32*kb + 8*(e/4) + 4*hl + e%4 of query my_q.
+    const bool need_mask = (kv0 + kKTile > N) || (kCausal && kv0 + kKTile - 1 > q_row0);
+    const int base = kv0 + 4 * hl;
+    uint32_t pd[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float ds2[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + i], a.c2, -l2));
+          if (need_mask) {
+            const int key = base + 32 * kb + 8 * ((e + i) >> 2) + ((e + i) & 3);
+            const bool ok = key < N && (!kCausal || key <= my_q);
+            x = ok ? x : 0.f;
+          }
+          ds2[i] = x * (dp[kb][e + i] - dd);
+        }
+        pd[kb][e >> 1] = E::pack2(ds2[0], ds2[1]);
+      }
+    }
+    // dQ^T += K^T dS^T over the four 16-key k-steps.
+#pragma unroll
+    for (int c = 0; c < kKTile / 16; ++c) {
+      const V8 bd = __builtin_bit_cast(V8, u32x4{pd[c >> 1][4 * (c & 1) + 0], pd[c >> 1][4 * (c & 1) + 1],
+                                                 pd[c >> 1][4 * (c & 1) + 2], pd[c >> 1][4 * (c & 1) + 3]});
+      const int r1 = 16 * c + 4 * (tg >> 1) + (tl >> 2);
+      const int r2 = r1 + 8;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int dim = 32 * db + 16 * (tg & 1) + 4 * (tl & 3);
+        const uint32_t o1 = tile_byte<D>(r1, dim >> 3) + 8 * ((dim >> 2) & 1);
+        const uint32_t o2 = tile_byte<D>(r2, dim >> 3) + 8 * ((dim >> 2) & 1);
+        const u32x2 k1 = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tk + o1)));
+        const u32x2 k2 = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tk + o2)));
+        dqt[db] = E::mfma(__builtin_bit_cast(V8, u32x4{k1[0], k1[1], k2[0], k2[1]}), bd, dqt[db]);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (my_q < N) {
+    uint16_t* qp = a.dq + head_off + (int64_t)my_q * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = 32 * db + 8 * r4 + 4 * hl;
+        *(u32x2*)(qp + dim) = u32x2{E::pack2(dqt[db][4 * r4 + 0] * a.scale, dqt[db][4 * r4 + 1] * a.scale),
+                                    E::pack2(dqt[db][4 * r4 + 2] * a.scale, dqt[db][4 * r4 + 3] * a.scale)};
+      }
+    }
+  }
+}
+
+}  // namespace bwd
+}  // namespace fa2

@@ -1,6 +1,6 @@
 /*
- * fa2.h -- C ABI of the fused exact-attention forward pass for AMD Instinct
- * MI355X (gfx950).
+ * fa2.h -- C ABI of fused exact attention for AMD Instinct MI355X (gfx950):
+ * the forward pass and its gradients.
  *
  * The operation.  For every batch b < B, head h < H and query row r < N:
  *
@@ -48,7 +48,7 @@ typedef enum {
   FA2_ERR_DTYPE = 4,   /* dtype is not a fa2_dtype value */
   FA2_ERR_SCALE = 5,   /* scale is NaN, infinite, or so large that scale*log2(e) overflows */
   FA2_ERR_ALIGN = 6,   /* a pointer is not 16-byte aligned */
-  FA2_ERR_ALIAS = 7,   /* o or lse overlaps an input, or o overlaps lse */
+  FA2_ERR_ALIAS = 7,   /* an output overlaps an input or another output */
   FA2_ERR_DEVICE = 8,  /* no current HIP device, or it is not a gfx950 */
   FA2_ERR_LAUNCH = 9   /* the HIP launch itself reported an error */
 } fa2_status;
@@ -86,11 +86,48 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             int64_t B, int64_t H, int64_t N, int64_t d,
             int causal, float scale, int dtype, void* stream);
 
+/*
+ * fa2_bwd -- enqueue the gradients of fa2_fwd on `stream` and return without
+ * waiting.  For a scalar loss with gradient dO = dL/dO, with P the softmax
+ * weights of the forward pass (masked pairs have P = 0) and s = scale * q.k:
+ *
+ *   D[b,h,r]  = sum_t dO[b,h,r,t] * O[b,h,r,t]
+ *   dS        = P o (dO V^T - D)              (row by row)
+ *   dQ = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO
+ *
+ *  - P is recomputed from the forward's logsumexp, P = exp(s - lse): "6.2
+ *    FlashAttention V2 in depth", section 7.1; "Flash Attention: Memory-
+ *    Efficient Attention at Scale", section "Recomputation in the backward pass".
+ *  - dS = P o (dP - D) with D = rowsum(dO o O), D computed by a preprocess step
+ *    for all rows first: "6.2 FlashAttention V2 in depth", section 7.3.
+ *  - Key/value tiles outside, query tiles inside, so dK and dV need no atomic
+ *    adds; dQ is gathered by a second pass instead of atomics (same page,
+ *    section 7.2).
+ *
+ * q, k, v     : the forward's inputs ([B, H, N, d], `dtype`).  Read only.
+ * o, lse      : the forward's outputs for the same q, k, v, causal, scale
+ *               (o: [B, H, N, d] `dtype`; lse: [B, H, N] float32).  Read only.
+ * dout        : dO, [B, H, N, d] `dtype`.  Read only.
+ * delta       : [B, H, N] float32 work array owned by the caller; overwritten
+ *               with D (its contents on return are D).
+ * dq, dk, dv  : [B, H, N, d] `dtype`; written.
+ * B, H, N, d, causal, scale, dtype, stream: as for fa2_fwd.
+ *
+ * Layout, alignment (16 bytes, every pointer), ownership, error reporting and
+ * the empty-problem rule are those of fa2_fwd; delta, dq, dk, dv must not
+ * overlap each other or any input.  The three kernels (D, then dK/dV, then dQ)
+ * run in order on `stream`; results are bitwise reproducible (no atomics).
+ */
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+            const float* lse, float* delta, void* dq, void* dk, void* dv,
+            int64_t B, int64_t H, int64_t N, int64_t d,
+            int causal, float scale, int dtype, void* stream);
+
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char* fa2_status_str(int status);
 
-/* Last HIP error code seen by a failing fa2_fwd call on this thread (0 if none);
- * useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
+/* Last HIP error code seen by a failing fa2_fwd or fa2_bwd call on this thread
+ * (0 if none); useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
 int fa2_last_hip_error(void);
 
 #ifdef __cplusplus

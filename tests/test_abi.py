@@ -114,3 +114,55 @@ def test_python_forward_rejects_bad_tensors(lib):
         fa.forward(q, q, q[:, :, :4])
     with pytest.raises(TypeError):
         fa.forward(q.float(), q.float(), q.float())
+
+
+# --- fa2_bwd ----------------------------------------------------------------------
+
+DO, DL, DQ, DK, DV = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+
+
+def _bwd(B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=0, q=Q, k=K, v=V, o=O, dout=DO, lse=L,
+         delta=DL, dq=DQ, dk=DK, dv=DV):
+    return fa.fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(B=-1), fa.FA2_ERR_SHAPE), (dict(N=-3), fa.FA2_ERR_SHAPE), (dict(N=2 ** 31), fa.FA2_ERR_SHAPE),
+    (dict(B=2 ** 20, H=2 ** 20, N=1024), fa.FA2_ERR_SHAPE),
+    (dict(d=32), fa.FA2_ERR_HEADDIM), (dict(d=512), fa.FA2_ERR_HEADDIM),
+    (dict(dtype=3), fa.FA2_ERR_DTYPE),
+    (dict(scale=math.nan), fa.FA2_ERR_SCALE), (dict(scale=3.0e38), fa.FA2_ERR_SCALE),
+    (dict(q=0), fa.FA2_ERR_NULLPTR), (dict(o=0), fa.FA2_ERR_NULLPTR), (dict(dout=0), fa.FA2_ERR_NULLPTR),
+    (dict(lse=0), fa.FA2_ERR_NULLPTR), (dict(delta=0), fa.FA2_ERR_NULLPTR), (dict(dq=0), fa.FA2_ERR_NULLPTR),
+    (dict(dk=0), fa.FA2_ERR_NULLPTR), (dict(dv=0), fa.FA2_ERR_NULLPTR),
+    (dict(dout=DO + 8), fa.FA2_ERR_ALIGN), (dict(delta=DL + 4), fa.FA2_ERR_ALIGN), (dict(dv=DV + 2), fa.FA2_ERR_ALIGN),
+    (dict(dq=Q), fa.FA2_ERR_ALIAS), (dict(dk=O + 512), fa.FA2_ERR_ALIAS), (dict(dv=DO + 16), fa.FA2_ERR_ALIAS),
+    (dict(delta=L), fa.FA2_ERR_ALIAS), (dict(dq=DK), fa.FA2_ERR_ALIAS), (dict(delta=DV + 1024), fa.FA2_ERR_ALIAS),
+])
+def test_bwd_argument_checks(lib, kwargs, code):
+    assert _bwd(**kwargs) == code
+
+
+@pytest.mark.parametrize("kwargs", [dict(B=0), dict(N=0), dict(H=0, q=0, dq=0, delta=0)])
+def test_bwd_empty_problem_is_a_no_op(lib, kwargs):
+    assert _bwd(**kwargs) == fa.FA2_OK
+
+
+def test_bwd_valid_call_without_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    for d in (64, 128, 256):
+        assert _bwd(d=d, dtype=1, causal=1, N=333) == fa.FA2_ERR_DEVICE
+
+
+def test_python_backward_rejects_bad_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q, q, lse)  # host tensors
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q, q[:, :, :4], lse)
+    with pytest.raises(TypeError):
+        fa.backward(q, q, q, q, q.float(), lse)

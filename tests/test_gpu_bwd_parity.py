@@ -1,0 +1,114 @@
+"""GPU parity of the gradients: fa2_bwd through the C ABI against the fp64
+gradient oracle (oracle/attention_bwd_ref.c), on the GPU forward pass's own O
+and L (the way the two calls are used together).
+
+Tolerance (relative to the largest magnitude of each reference gradient, plus a
+small absolute floor): the GPU rounds P and dS to the input type before their
+products (unit roundoff u = 2^-11 fp16, 2^-8 bf16), reads O rounded to the input
+type for D and rounds the outputs once; each of those contributes at most about
+u * max|gradient| to an element, so the bound is 4u relative.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_11_amd as fa
+import oracle
+from exact_attention_11_amd.inputs import make_qkv
+
+pytestmark = pytest.mark.gpu
+
+UNIT = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
+REL = 4.0
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()
+
+
+def _dout(shape, dtype, seed):
+    g = torch.Generator().manual_seed(1000 + seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def _run(q, k, v, do, causal, scale):
+    qc, kc, vc, gc = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.forward(qc, kc, vc, causal=causal, scale=scale)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = fa.backward(qc, kc, vc, o, gc, lse, causal=causal, scale=scale, delta=delta)
+    torch.cuda.synchronize()
+    return o.cpu(), dq.cpu(), dk.cpu(), dv.cpu(), delta.cpu()
+
+
+def _check(name, got, ref, dtype, what):
+    got = got.double().numpy()
+    assert np.all(np.isfinite(got)), (what, name, "non-finite")
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    tol = REL * UNIT[dtype] * scale + 1e-6
+    _log(f"  {what} {name}: max|d|={err:.3e} max|ref|={scale:.3e} rel={err / max(scale, 1e-30):.2e} tol={tol:.2e}")
+    assert err <= tol, (what, name, err, tol)
+
+
+def _parity(B, H, N, d, dtype, causal, scale=None, seed=0, dist="normal"):
+    q, k, v = make_qkv(B, H, N, d, dtype, dist, seed)
+    do = _dout((B, H, N, d), dtype, seed)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    what = f"B={B} H={H} N={N} d={d} {dtype} causal={causal} scale={scale}"
+    _log(f"case {what}")
+    o, dq, dk, dv, delta = _run(q, k, v, do, causal, scale)
+    s32 = float(np.float32(scale))
+    rq, rk, rv, _ = oracle.attention_bwd_f64(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                             do.double().numpy(), causal, s32)
+    _check("dQ", dq, rq, dtype, what)
+    _check("dK", dk, rk, dtype, what)
+    _check("dV", dv, rv, dtype, what)
+    # D is the row sum of dO o O over the GPU's own O, accumulated in fp32.
+    want = (do.double() * o.double()).sum(-1).numpy()
+    err = float(np.max(np.abs(delta.double().numpy() - want)))
+    assert err <= 1e-5 * max(1.0, float(np.max(np.abs(want)))), (what, "D", err)
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 128, 129, 200, 257])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
+def test_bwd_parity_ragged_sweep(dtype, d, causal, N):
+    _parity(1, 2, N, d, dtype, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
+def test_bwd_parity_medium(dtype, causal):
+    _parity(2, 3, 700, 128, dtype, causal, seed=4)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
+def test_bwd_parity_unusual_scales(scale):
+    _parity(1, 2, 300, 64, torch.float16, True, scale=scale, seed=6)
+
+
+def test_bwd_zero_scale_closed_form():
+    """Multiplier 0: dQ and dK vanish exactly."""
+    q, k, v = make_qkv(1, 1, 130, 64, torch.float16, "normal", 2)
+    do = _dout(q.shape, torch.float16, 2)
+    _, dq, dk, _, _ = _run(q, k, v, do, True, 0.0)
+    assert torch.all(dq == 0) and torch.all(dk == 0)
+
+
+def test_bwd_deterministic_bitwise():
+    q, k, v = make_qkv(2, 2, 333, 128, torch.bfloat16, "normal", 3)
+    do = _dout(q.shape, torch.bfloat16, 3)
+    a = _run(q, k, v, do, True, 0.1)
+    b = _run(q, k, v, do, True, 0.1)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -30,8 +30,12 @@ if ROOT not in sys.path:
 PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
 DEFAULT_WORKLOAD = "b1h32_n16384_d128_causal"
 PROFILES = os.path.join(ROOT, "profiles")
+# The sources that define the kernels of each pass (a recorded profile applies
+# while their digest is unchanged).
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
-                  for f in ("fa2_common.h", "fa2_fwd_4wave.h", "fa2_fwd_8wave.h", "fa2_api.hip")]
+                  for f in ("fa2_common.h", "fa2_fwd_4wave.h", "fa2_fwd_8wave.h")]
+BWD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
+                      for f in ("fa2_common.h", "fa2_bwd.h")]
 
 
 def log(msg: str) -> None:
@@ -43,9 +47,9 @@ def flop_count(B: int, H: int, N: int, d: int, causal: bool) -> float:
     return f / 2.0 if causal else f
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -128,6 +132,37 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
     }
 
 
+def cpu_baseline_bwd(w, q, k, v, dout, target_s: float = 12.0):
+    """Time the fp64 gradient oracle on whole heads of the workload, a batch of
+    one head per host thread at a time (the oracle works a head per thread),
+    until the sample has taken about ``target_s`` seconds (at least one batch)."""
+    import numpy as np
+
+    import oracle
+
+    threads = host_threads()
+    scale = float(np.float32(w.scale))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    flop_head = 2.5 * flop_count(1, 1, w.N, w.d, w.causal)
+    secs, n, used = 0.0, 0, 1
+    while n < len(heads) and secs < target_s:
+        batch = heads[n:n + threads]
+        args = [np.stack([t[b, h].double().numpy() for (b, h) in batch])[None] for t in (q, k, v, dout)]
+        t0 = time.perf_counter()
+        oracle.attention_bwd_f64(*args, w.causal, scale, nthreads=threads)
+        secs += time.perf_counter() - t0
+        n += len(batch)
+        used = max(used, len(batch))
+    return {
+        "value": n * flop_head / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": used,
+        "kind": "oracle",
+        "sample": f"{n} whole head(s) of {w.name}: {n * flop_head / 1e9:.1f} GFLOP in {secs:.1f} s "
+                  f"(fp64 gradient oracle)",
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +171,8 @@ def main() -> int:
     ap.add_argument("--min-warmup-ms", type=float, default=300.0,
                     help="extra untimed steps until the warm-up has lasted this long (clock ramp-up)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward pass (the headline) or the gradient pass of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -167,15 +204,35 @@ def main() -> int:
     from exact_attention_11_amd.inputs import WORKLOADS, workload_inputs
 
     w = WORKLOADS[args.workload]
-    log(f"workload {w.name}: {w.what}")
+    log(f"workload {w.name}: {w.what} ({args.pass_} pass)")
     q, k, v = workload_inputs(w, seed=0)
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
     o = torch.empty_like(dq)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
+    if args.pass_ == "fwd":
+        def step():
+            fa.forward(dq, dk, dv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        flop = flop_count(w.B, w.H, w.N, w.d, w.causal)
+        metric = "attention fwd TFLOP/s and % of MI355X FP16/BF16 MFMA peak, hd128 seq 2k-16k"
+    else:
+        # The gradient pass of the same problem: its inputs are the forward's O and
+        # L and a seeded dO.
         fa.forward(dq, dk, dv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        g = torch.Generator().manual_seed(1)
+        dout_h = torch.randn((w.B, w.H, w.N, w.d), generator=g).to(q.dtype)
+        dout = dout_h.cuda()
+        delta = torch.empty_like(lse)
+        gq, gk, gv = torch.empty_like(dq), torch.empty_like(dq), torch.empty_like(dq)
+
+        def step():
+            fa.backward(dq, dk, dv, o, dout, lse, causal=w.causal, scale=w.scale, stream=stream, delta=delta,
+                        dq=gq, dk=gk, dv=gv)
+        # Conventional count: five N x N x d products per (query, key) pair (S, dP,
+        # dV, dQ, dK), 2.5x the forward's.
+        flop = 2.5 * flop_count(w.B, w.H, w.N, w.d, w.causal)
+        metric = "attention bwd TFLOP/s (5 products per pair) and % of MI355X FP16/BF16 MFMA peak"
 
     for _ in range(args.warmup):
         step()
@@ -205,15 +262,14 @@ def main() -> int:
     total_ms = starts[0].elapsed_time(ends[-1])
     ms_per_step = total_ms / args.steps
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
-    flop = flop_count(w.B, w.H, w.N, w.d, w.causal)
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
     log(f"{args.steps} steps: {ms_per_step:.4f} ms/step (events), launch avg {avg_launch_ms:.4f} ms, "
         f"min {min(launch_ms):.4f} ms, wall {wall_s * 1e3 / args.steps:.4f} ms/step -> {value:.1f} TFLOP/s")
 
-    traffic = recorded_traffic(w.name)
+    traffic = recorded_traffic(w.name) if args.pass_ == "fwd" else None
     result = {
-        "metric": "attention fwd TFLOP/s and % of MI355X FP16/BF16 MFMA peak, hd128 seq 2k-16k",
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -226,8 +282,10 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "inputs": w.dist, "flop_per_step": flop, "kernel_source_digest": kernel_source_digest()},
+        "config": {"workload": w.name, "pass": args.pass_, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "inputs": w.dist, "flop_per_step": flop,
+                   "kernel_source_digest": kernel_source_digest(
+                       KERNEL_SOURCES if args.pass_ == "fwd" else BWD_KERNEL_SOURCES)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
                      "traffic": traffic},
@@ -235,7 +293,10 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the workload ...")
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        if args.pass_ == "fwd":
+            result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        else:
+            result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, dout_h, args.cpu_seconds)
         log(f"cpu baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
     return 0

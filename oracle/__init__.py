@@ -11,6 +11,10 @@ Contents
     natural-log logsumexp per row) in fp64, implemented in ``attention_ref.c``
     and loaded through ctypes.  See that file's header for the passages of the
     pages it follows.
+``attention_masked_f64``
+    The same definition under a general mask (sliding window, a prefix visible
+    to every query, document segment ids), implemented in
+    ``attention_mask_ref.c``.
 ``attention_bwd_f64``
     The gradients dQ, dK, dV of that definition for a given dO (and the row
     statistic D), by the chain rule in fp64, implemented in
@@ -35,16 +39,17 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attention_ref.c")
 _BWD_SRC = os.path.join(_HERE, "attention_bwd_ref.c")
+_MASK_SRC = os.path.join(_HERE, "attention_mask_ref.c")
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 _lib_cache: dict[str, ctypes.CDLL] = {}
 
 
-def build(src: str = _SRC, out: str = LIB_PATH, bwd_src: str = _BWD_SRC) -> str:
-    """Compile the C oracle (forward and gradient sources) with gcc (no
-    fast-math: IEEE fp64 throughout)."""
+def build(src: str = _SRC, out: str = LIB_PATH, bwd_src: str = _BWD_SRC, mask_src: str = _MASK_SRC) -> str:
+    """Compile the C oracle (forward, gradient and general-mask sources) with
+    gcc (no fast-math: IEEE fp64 throughout)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-           "-ffp-contract=off", "-pthread", src, bwd_src, "-o", out, "-lm"]
+           "-ffp-contract=off", "-pthread", src, bwd_src, mask_src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -70,6 +75,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oracle_attention_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
                                              ctypes.c_int, ctypes.c_double, ctypes.c_int]
     lib.oracle_attention_bwd_f64.restype = ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.oracle_attention_masked_f64.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64, i64, ip,
+                                                ctypes.c_double, ctypes.c_int]
+    lib.oracle_attention_masked_f64.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
 
@@ -177,3 +186,38 @@ def attention_bwd_f64(q, k, v, dout, causal: bool, scale: float, nthreads: int |
     if squeeze:
         return dq[0, 0], dk[0, 0], dv[0, 0], delta[0, 0]
     return dq, dk, dv, delta
+
+
+def attention_masked_f64(q, k, v, scale: float, window_left: int = -1, window_right: int = -1,
+                         prefix: int = 0, segment_ids=None, causal: bool = False,
+                         nthreads: int | None = None, lib_path: str = LIB_PATH):
+    """Exact attention over [B, H, N, d] fp64 arrays under a general mask.
+
+    Key c is allowed for query r when c < N, ``segment_ids[b, c] ==
+    segment_ids[b, r]`` (if given, an int array [B, N]), and either c < prefix
+    or r - window_left <= c <= r + window_right (a negative bound is
+    unbounded).  ``causal`` is window_right = 0 (combined with a given
+    window_right by taking the smaller bound).  Returns ``(o, lse)``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if not (q.shape == k.shape == v.shape) or q.ndim != 4:
+        raise ValueError("expected three [B, H, N, d] arrays of equal shape")
+    B, H, N, d = q.shape
+    wr = int(window_right)
+    if causal:
+        wr = 0 if wr < 0 else min(wr, 0)
+    seg_ptr = None
+    if segment_ids is not None:
+        seg = np.ascontiguousarray(np.asarray(segment_ids, dtype=np.int32))
+        if seg.shape != (B, N):
+            raise ValueError("segment_ids must be [B, N]")
+        seg_ptr = seg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    lib = load(lib_path)
+    rc = lib.oracle_attention_masked_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                         int(window_left), wr, int(prefix), seg_ptr, float(scale),
+                                         _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_masked_f64 failed with code {rc}")
+    return o, lse

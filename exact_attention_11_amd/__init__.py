@@ -35,9 +35,16 @@ FA2_ERR_ALIGN = 6
 FA2_ERR_ALIAS = 7
 FA2_ERR_DEVICE = 8
 FA2_ERR_LAUNCH = 9
+FA2_ERR_MASK = 10
 
 # Every symbol include/fa2.h declares.
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_bwd", "fa2_status_str", "fa2_last_hip_error")
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_bwd", "fa2_status_str", "fa2_last_hip_error")
+
+
+class Fa2Mask(ctypes.Structure):
+    """The C struct fa2_mask of include/fa2.h."""
+    _fields_ = [("causal", ctypes.c_int), ("window_left", ctypes.c_int64), ("window_right", ctypes.c_int64),
+                ("prefix", ctypes.c_int64), ("segment_ids", ctypes.c_void_p)]
 
 HEAD_DIMS = (64, 128, 256)
 
@@ -69,6 +76,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                             ctypes.c_int, vp]
     lib.fa2_fwd.restype = ctypes.c_int
+    lib.fa2_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.POINTER(Fa2Mask),
+                                   ctypes.c_float, ctypes.c_int, vp]
+    lib.fa2_fwd_masked.restype = ctypes.c_int
     lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                             ctypes.c_float, ctypes.c_int, vp]
     lib.fa2_bwd.restype = ctypes.c_int
@@ -86,6 +96,13 @@ def fa2_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d:
     """Direct call of the C entry point with raw device addresses; returns the status."""
     return load_library().fa2_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), int(dtype),
                                   stream)
+
+
+def fa2_fwd_masked(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, mask,
+                   scale: float, dtype: int, stream: int) -> int:
+    """Direct call of the masked forward entry point (mask: a Fa2Mask or None)."""
+    ptr = ctypes.byref(mask) if mask is not None else None
+    return load_library().fa2_fwd_masked(q, k, v, o, lse, B, H, N, d, ptr, float(scale), int(dtype), stream)
 
 
 def fa2_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, delta: int, dq: int, dk: int, dv: int,
@@ -113,12 +130,15 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
 
 
-def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None):
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None,
+            window=None, prefix: int = 0, segment_ids=None):
     """Attention forward on the GPU.  Returns ``(o, lse)``.
 
     ``scale`` defaults to 1/sqrt(d) (computed here, not in the library).  ``out``
     and ``lse`` may be given preallocated; ``stream`` defaults to torch's current
-    stream of the tensors' device.
+    stream of the tensors' device.  A general mask: ``window=(left, right)``
+    (-1 for no bound), ``prefix`` (keys below it visible to every query of the
+    same segment) and ``segment_ids`` (an int32 [B, N] tensor on the device).
     """
     import torch
 
@@ -143,10 +163,24 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         raise ValueError("out must be a contiguous tensor like q")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    general = window is not None or prefix or segment_ids is not None
+    if general:
+        wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+        seg_ptr = None
+        if segment_ids is not None:
+            if (segment_ids.shape != (B, N) or segment_ids.dtype != torch.int32 or not segment_ids.is_contiguous()
+                    or segment_ids.device != q.device):
+                raise ValueError("segment_ids must be a contiguous int32 [B, N] tensor on q's device")
+            seg_ptr = segment_ids.data_ptr()
+        mask = Fa2Mask(int(bool(causal)), wl, wr, int(prefix), seg_ptr)
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        rc = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                     B, H, N, d, int(bool(causal)), float(scale), code, s.cuda_stream)
+        if general:
+            rc = fa2_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                B, H, N, d, mask, float(scale), code, s.cuda_stream)
+        else:
+            rc = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, H, N, d, int(bool(causal)), float(scale), code, s.cuda_stream)
     if rc != FA2_OK:
         raise Fa2Error(rc, fa2_status_str(rc))
     return out, lse

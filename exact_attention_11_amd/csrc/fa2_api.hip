@@ -54,29 +54,33 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
 // Query rows per workgroup of the kernel that serves head dim d.
 int64_t rows_per_workgroup(int64_t d) { return d == 256 ? fa2::w4::kBr : fa2::w8::kBr; }
 
-template <int kDType, int D, bool kCausal>
+template <int kDType, int D, int kMask>
 hipError_t launch(const fa2::FwdArgs& args, hipStream_t stream) {
   if constexpr (D == 256) {
-    hipLaunchKernelGGL((fa2::w4::fa2_fwd_4wave<kDType, D, kCausal>), dim3(args.n_wg), dim3(fa2::w4::kThreads), 0,
+    hipLaunchKernelGGL((fa2::w4::fa2_fwd_4wave<kDType, D, kMask>), dim3(args.n_wg), dim3(fa2::w4::kThreads), 0,
                        stream, args);
   } else {
-    hipLaunchKernelGGL((fa2::w8::fa2_fwd_8wave<kDType, D, kCausal>), dim3(args.n_wg), dim3(fa2::w8::kThreads), 0,
+    hipLaunchKernelGGL((fa2::w8::fa2_fwd_8wave<kDType, D, kMask>), dim3(args.n_wg), dim3(fa2::w8::kThreads), 0,
                        stream, args);
   }
   return hipGetLastError();
 }
 
 template <int kDType, int D>
-hipError_t launch_c(const fa2::FwdArgs& args, bool causal, hipStream_t stream) {
-  return causal ? launch<kDType, D, true>(args, stream) : launch<kDType, D, false>(args, stream);
+hipError_t launch_m(const fa2::FwdArgs& args, int mask_mode, hipStream_t stream) {
+  switch (mask_mode) {
+    case fa2::kMaskNone: return launch<kDType, D, fa2::kMaskNone>(args, stream);
+    case fa2::kMaskCausal: return launch<kDType, D, fa2::kMaskCausal>(args, stream);
+    default: return launch<kDType, D, fa2::kMaskGeneral>(args, stream);
+  }
 }
 
 template <int kDType>
-hipError_t launch_d(const fa2::FwdArgs& args, int64_t d, bool causal, hipStream_t stream) {
+hipError_t launch_d(const fa2::FwdArgs& args, int64_t d, int mask_mode, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_c<kDType, 64>(args, causal, stream);
-    case 128: return launch_c<kDType, 128>(args, causal, stream);
-    default: return launch_c<kDType, 256>(args, causal, stream);
+    case 64: return launch_m<kDType, 64>(args, mask_mode, stream);
+    case 128: return launch_m<kDType, 128>(args, mask_mode, stream);
+    default: return launch_m<kDType, 256>(args, mask_mode, stream);
   }
 }
 
@@ -124,14 +128,15 @@ const char* fa2_status_str(int status) {
     case FA2_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA2_ERR_DEVICE: return "no usable gfx950 device";
     case FA2_ERR_LAUNCH: return "kernel launch failed";
+    case FA2_ERR_MASK: return "mask: window bound below -1, negative prefix or misaligned segment ids";
     default: return "unknown status";
   }
 }
 
 int fa2_last_hip_error(void) { return g_last_hip_error; }
 
-int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-            int64_t d, int causal, float scale, int dtype, void* stream) {
+int fa2_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t N, int64_t d, const fa2_mask* mask, float scale, int dtype, void* stream) {
   g_last_hip_error = 0;
   // ---- argument checks: no HIP call before they all pass -------------------
   if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
@@ -139,6 +144,10 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
   const float c2 = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
+  fa2_mask m = {0, -1, -1, 0, nullptr};
+  if (mask) m = *mask;
+  if (m.window_left < -1 || m.window_right < -1 || m.prefix < 0) return FA2_ERR_MASK;
+  if (((uintptr_t)m.segment_ids) & 3) return FA2_ERR_MASK;
   if (B == 0 || H == 0 || N == 0) return FA2_OK;  // empty problem: nothing to do
   // Index limits: rows fit in int32 inside the kernel, the grid in 2^31 - 1
   // workgroups, byte sizes in 63 bits.
@@ -158,6 +167,29 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
       overlaps(lse, lse_bytes, k, tensor_bytes) || overlaps(lse, lse_bytes, v, tensor_bytes) ||
       overlaps(o, tensor_bytes, lse, lse_bytes))
     return FA2_ERR_ALIAS;
+  if (m.segment_ids) {
+    const uint64_t seg_bytes = (uint64_t)(B * N) * 4;
+    if (overlaps(m.segment_ids, seg_bytes, o, tensor_bytes) || overlaps(m.segment_ids, seg_bytes, lse, lse_bytes))
+      return FA2_ERR_ALIAS;
+  }
+
+  // ---- mask: fold the causal flag into the right bound, drop bounds that
+  // cannot bite, and pick the kernel's mask mode -----------------------------
+  int64_t wl = m.window_left, wr = m.window_right, prefix = m.prefix;
+  if (m.causal) wr = 0;  // key <= query, whatever right bound was given
+  if (wl >= N - 1) wl = -1;  // r - wl <= 0 for every row
+  if (wr >= N - 1) wr = -1;
+  if (prefix >= N) {  // every key is in the prefix: the window no longer matters
+    wl = -1;
+    wr = -1;
+    prefix = 0;
+  }
+  if (wl < 0 && wr < 0) prefix = 0;  // the window admits every key already
+  int mode = fa2::kMaskGeneral;
+  if (!m.segment_ids && prefix == 0 && wl < 0) {
+    if (wr < 0) mode = fa2::kMaskNone;
+    else if (wr == 0) mode = fa2::kMaskCausal;
+  }
 
   // ---- device ---------------------------------------------------------------
   const int dev_status = check_device();
@@ -173,14 +205,25 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   args.n_qtiles = (int)n_qtiles;
   args.n_wg = (int)(bh * n_qtiles);
   args.c2 = c2;
+  args.wl = (int)wl;
+  args.wr = (int)wr;
+  args.prefix = (int)prefix;
+  args.H = (int)H;
+  args.seg = m.segment_ids;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_d<0>(args, d, causal != 0, s) : launch_d<1>(args, d, causal != 0, s);
+  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_d<0>(args, d, mode, s) : launch_d<1>(args, d, mode, s);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FA2_ERR_LAUNCH;
   }
   return FA2_OK;
+}
+
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+            int64_t d, int causal, float scale, int dtype, void* stream) {
+  const fa2_mask m = {causal != 0, -1, -1, 0, nullptr};
+  return fa2_fwd_masked(q, k, v, o, lse, B, H, N, d, &m, scale, dtype, stream);
 }
 
 int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

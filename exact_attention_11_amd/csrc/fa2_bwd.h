@@ -112,12 +112,6 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2
   }
 }
 
-// One global_load_lds_dword: every lane copies 4 bytes to lds_base + 4 * lane.
-__device__ __forceinline__ void dma4(const void* g, FA2_LDS void* lds_base) {
-  const uint32_t m0v = (uint32_t)(size_t)lds_base;
-  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
-}
-
 template <int kDType> __device__ __forceinline__ float to_f32(uint16_t x) {
   if constexpr (kDType == 0) return (float)__builtin_bit_cast(_Float16, x);
   else return __uint_as_float((uint32_t)x << 16);

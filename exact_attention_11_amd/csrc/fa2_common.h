@@ -38,7 +38,20 @@ struct FwdArgs {
   int n_qtiles;  // ceil(N / query rows per workgroup)
   int n_wg;      // B * H * n_qtiles
   float c2;      // scale * log2(e)
+  // General mask (used by the kMaskGeneral instances only): key c is visible
+  // to query r iff c < N, seg[b, c] == seg[b, r] (when seg is given), and
+  // c < prefix or r - wl <= c <= r + wr (a negative bound is no bound).
+  int wl;
+  int wr;
+  int prefix;
+  int H;            // heads per batch: batch b = (b*H + h) / H
+  const int* seg;   // [B, N] segment ids, or nullptr
 };
+
+// Mask modes of the forward kernels.
+constexpr int kMaskNone = 0;
+constexpr int kMaskCausal = 1;
+constexpr int kMaskGeneral = 2;
 
 // Element-type specific pieces: the MFMA and the fp32 -> storage conversion.
 template <int kDType> struct Elem;
@@ -78,6 +91,12 @@ __device__ __forceinline__ void dma16(const void* g, FA2_LDS void* lds_base) {
 __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, FA2_LDS void* lds_base) {
   const uint32_t m0v = (uint32_t)(size_t)lds_base;
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0v) : "memory");
+}
+
+// One global_load_lds_dword: every lane copies 4 bytes to lds_base + 4 * lane.
+__device__ __forceinline__ void dma4(const void* g, FA2_LDS void* lds_base) {
+  const uint32_t m0v = (uint32_t)(size_t)lds_base;
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
 }
 
 // s_waitcnt vmcnt(n) followed by a workgroup barrier.  The explicit count lets

@@ -67,8 +67,10 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src_head,
   }
 }
 
-template <int kDType, int D, bool kCausal>
+template <int kDType, int D, int kMask>
 __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdArgs a) {
+  constexpr bool kCausal = kMask == kMaskCausal;
+  constexpr bool kGeneral = kMask == kMaskGeneral;
   typedef Elem<kDType> E;
   typedef typename E::V8 V8;
   constexpr int CPR = D / 8;
@@ -97,12 +99,31 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   const uint16_t* __restrict__ kh = a.k + head_off;
   const uint16_t* __restrict__ vh = a.v + head_off;
 
-  const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
-  const int nt = (kv_end + kBc - 1) / kBc;
+  // Key tiles t0 .. t_end - 1 are visited.
+  int t0 = 0, t_end;
+  if constexpr (kGeneral) {
+    const int q0 = qtile * kBr, q1 = min(N, q0 + kBr) - 1;
+    // Last visible key: the window's right edge, or the prefix's end if later.
+    const int hi = a.wr < 0 ? N - 1 : min(N - 1, max(q1 + a.wr, a.prefix - 1));
+    const int lo = (a.prefix > 0 || a.wl < 0) ? 0 : max(0, q0 - a.wl);
+    t0 = lo / kBc;
+    t_end = hi / kBc + 1;
+  } else {
+    const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
+    t_end = (kv_end + kBc - 1) / kBc;
+  }
+  const int* __restrict__ segb = nullptr;  // this batch's segment ids
+  int seg_q = 0;
+  if constexpr (kGeneral) {
+    if (a.seg) {
+      segb = a.seg + (int64_t)(bh / a.H) * N;
+      seg_q = segb[min(my_q, N - 1)];
+    }
+  }
 
   // First K and V tiles start streaming before anything else.
-  load_tile<D, false>(kh, sK, 0, N, wave, lane);
-  load_tile<D, true>(vh, sV, 0, N, wave, lane);
+  load_tile<D, false>(kh, sK, t0 * kBc, N, wave, lane);
+  load_tile<D, true>(vh, sV, t0 * kBc, N, wave, lane);
 
   // Q fragments (B operand of S^T = K Q^T), loaded once and kept in registers.
   // They are consumed right here so that the compiler's own wait for them
@@ -122,11 +143,17 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   float m_run = kNegInf;  // reference max of this lane's query row (log2 units)
   float l_part = 0.f;     // this lane's share of the row sum
 
-  for (int j = 0; j < nt; ++j) {
+  for (int j = t0; j < t_end; ++j) {
     const int kv0 = j * kBc;
     // Wave-uniform classification of this tile for this wave's 32 rows.
-    const bool active = !kCausal || kv0 <= q_row0 + 31;
-    const bool need_mask = (kv0 + kBc > N) || (kCausal && kv0 + kBc - 1 > q_row0);
+    bool active = !kCausal || kv0 <= q_row0 + 31;
+    bool need_mask = (kv0 + kBc > N) || (kCausal && kv0 + kBc - 1 > q_row0);
+    if constexpr (kGeneral) {
+      const int k1 = kv0 + kBc - 1, qa = q_row0, qb = q_row0 + 31;
+      active = !(kv0 >= a.prefix && ((a.wr >= 0 && kv0 > qb + a.wr) || (a.wl >= 0 && k1 < qa - a.wl)));
+      need_mask = !(k1 < N && !segb &&
+                    (k1 < a.prefix || ((a.wl < 0 || kv0 >= qb - a.wl) && (a.wr < 0 || k1 <= qa + a.wr))));
+    }
     const bool generic = need_mask || !(a.c2 > 0.f);
 
     wait_vm_barrier<kLoads>();  // K_j has landed (V_j may still be in flight)
@@ -148,7 +175,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
     // The prefetch is issued on every step (the last step re-reads its own
     // tile, which nobody consumes) so that the number of loads in flight is the
     // same on every path through the loop.
-    const int kv_next = j + 1 < nt ? kv0 + kBc : kv0;
+    const int kv_next = j + 1 < t_end ? kv0 + kBc : kv0;
     load_tile<D, false>(kh, sK, kv_next, N, wave, lane);
 
     uint32_t pk[2][8];  // probabilities, packed pairs, B-operand order
@@ -161,7 +188,12 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool masked = key >= N || (kCausal && key > my_q);
+            bool masked = key >= N || (kCausal && key > my_q);
+            if constexpr (kGeneral) {
+              masked = key >= N ||
+                       !(key < a.prefix || ((a.wl < 0 || key >= my_q - a.wl) && (a.wr < 0 || key <= my_q + a.wr)));
+              if (segb) masked = masked || segb[min(key, N - 1)] != seg_q;
+            }
             const float t = s[kb][r] * a.c2;
             s[kb][r] = masked ? kNegInf : t;
           }

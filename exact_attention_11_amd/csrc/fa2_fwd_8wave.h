@@ -85,8 +85,10 @@ template <int CPR> __device__ __forceinline__ uint32_t vs_byte(int row, int chun
   return (uint32_t)((((row >> 4) * CPR + chunk) << 8) + ((((row & 15) ^ (4 * (chunk & 3)))) << 4));
 }
 
-template <int kDType, int D, bool kCausal>
+template <int kDType, int D, int kMask>
 __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
+  constexpr bool kCausal = kMask == kMaskCausal;
+  constexpr bool kGeneral = kMask == kMaskGeneral;
   typedef Elem<kDType> E;
   typedef typename E::V8 V8;
   constexpr int CPR = D / 8;                          // 16-byte chunks per K/V row
@@ -98,11 +100,17 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   constexpr float kNegInf = -__builtin_huge_valf();
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(kLoads >= 1 && kLoads * 64 * kWaves == kBc * CPR, "tile copy split");
+  // Copy instructions per wave per tile: K and V, plus the keys' segment ids
+  // under a general mask (issued by every wave, so the counts stay uniform).
+  constexpr int kTileLoads = 2 * kLoads + (kGeneral ? 1 : 0);
+  constexpr int kSegSlots = 4;  // segment ids of tiles st..st+2 stay readable while group 1 reads st-1
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem_[(kKSlots + kVSlots + kTSlots) * kTile];
   FA2_LDS uint16_t* const sK = (FA2_LDS uint16_t*)smem_;
   FA2_LDS uint16_t* const sVs = sK + kKSlots * kTile;
   FA2_LDS uint16_t* const sVt = sVs + kVSlots * kTile;
+  __shared__ __attribute__((aligned(16))) int seg_[kGeneral ? kSegSlots * kBc : 4];
+  FA2_LDS int* const sSeg = (FA2_LDS int*)seg_;
 
   const int N = a.N;
   int bh, qtile;
@@ -133,11 +141,37 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   const uint32_t voffK = (uint32_t)((sigma(kr) * D + cch * 8) * 2);
   const uint32_t voffV = (uint32_t)((vr * D + cch * 8) * 2);
 
-  const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
-  const int nt = (kv_end + kBc - 1) / kBc;
+  // Key tiles t0 .. t0 + nt - 1 are visited (step st handles tile t0 + st).
+  int t0 = 0, t_end;
+  if constexpr (kGeneral) {
+    const int q0 = qtile * kBr, q1 = min(N, q0 + kBr) - 1;
+    // Last visible key: the window's right edge, or the prefix's end if later.
+    const int hi = a.wr < 0 ? N - 1 : min(N - 1, max(q1 + a.wr, a.prefix - 1));
+    const int lo = (a.prefix > 0 || a.wl < 0) ? 0 : max(0, q0 - a.wl);
+    t0 = lo / kBc;
+    t_end = hi / kBc + 1;
+  } else {
+    const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
+    t_end = (kv_end + kBc - 1) / kBc;
+  }
+  const int nt = t_end - t0;
+  const int* __restrict__ segb = nullptr;  // this batch's segment ids
+  int seg_q = 0;                           // this lane's query's segment id
+  if constexpr (kGeneral) {
+    if (a.seg) {
+      segb = a.seg + (int64_t)(bh / a.H) * N;
+      seg_q = segb[min(my_q, N - 1)];
+    }
+  }
 
-  auto issue_tile = [&](int j, int slot) __attribute__((always_inline)) {
-    const int kv0 = j * kBc;
+  auto issue_tile = [&](int step, int slot) __attribute__((always_inline)) {
+    const int kv0 = (t0 + step) * kBc;
+    if constexpr (kGeneral) {
+      // Segment ids of the tile's keys (every wave copies the same 256 bytes;
+      // without segment ids the copy reads K and is never used).
+      const void* src = segb ? (const void*)(segb + min(kv0 + lane, N - 1)) : (const void*)kh;
+      dma4(src, sSeg + (step % kSegSlots) * kBc);
+    }
     FA2_LDS uint16_t* dk = sK + slot * kTile;
     FA2_LDS uint16_t* dv = sVs + slot * kTile;
     if (kv0 + kBc <= N) {
@@ -192,7 +226,17 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   f32x16 s[2];            // scores of one tile, between its S and softmax phases
   uint32_t pk[2][8];      // probabilities of one tile, between softmax and P.V
 
-  auto wave_active = [&](int j) __attribute__((always_inline)) { return !kCausal || j * kBc <= q_row0 + 31; };
+  // Tile classes for this wave's 32 rows: does any (row, key) pair survive the
+  // mask, and does every pair?
+  auto wave_active = [&](int step) __attribute__((always_inline)) {
+    const int k0 = (t0 + step) * kBc;
+    if constexpr (kGeneral) {
+      const int qa = q_row0, qb = q_row0 + 31;
+      return !(k0 >= a.prefix && ((a.wr >= 0 && k0 > qb + a.wr) || (a.wl >= 0 && k0 + kBc - 1 < qa - a.wl)));
+    } else {
+      return !kCausal || k0 <= q_row0 + 31;
+    }
+  };
 
   // Operand addresses: lane (hl, col) reads row 32*kb + col, chunk 2*ks + hl of
   // K, and column 32*db + col, chunk 2*c + hl of V^T.
@@ -318,11 +362,47 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   // too).  Otherwise (and always on the first tile) the tile's row max decides
   // whether the reference moves, O and l are rescaled by 2^(old - new), and the
   // weights are formed again.
-  auto softmax = [&](int j) __attribute__((always_inline)) {
-    const int kv0 = j * kBc;
-    const bool need_mask = (kv0 + kBc > N) || (kCausal && kv0 + kBc - 1 > q_row0);
+  auto softmax = [&](int step) __attribute__((always_inline)) {
+    const int kv0 = (t0 + step) * kBc;
+    bool need_mask = (kv0 + kBc > N) || (kCausal && kv0 + kBc - 1 > q_row0);
+    if constexpr (kGeneral) {
+      const int k1 = kv0 + kBc - 1, qa = q_row0, qb = q_row0 + 31;
+      const bool full = k1 < N && !segb &&
+                        (k1 < a.prefix || ((a.wl < 0 || kv0 >= qb - a.wl) && (a.wr < 0 || k1 <= qa + a.wr)));
+      need_mask = !full;
+    }
     float mul = a.c2;
-    if (need_mask) {
+    if (kGeneral && need_mask) {
+      // Key of element (kb, r) = kv0 + 8*hl + off with a constant off.
+      const int base = kv0 + 8 * hl;
+      const int lim_n = N - base;
+      const int lim_p = a.prefix - base;
+      const int lo_w = a.wl < 0 ? INT32_MIN / 2 : my_q - a.wl - base;
+      const int hi_w = a.wr < 0 ? INT32_MAX / 2 : my_q + a.wr - base;
+      const FA2_LDS int* sk = sSeg + (step % kSegSlots) * kBc + 8 * hl;
+      const bool pos = a.c2 > 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          u32x4 sg[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+          if (segb) {
+            sg[0] = *(const FA2_LDS u32x4*)(sk + 32 * kb + 16 * h8);
+            sg[1] = *(const FA2_LDS u32x4*)(sk + 32 * kb + 16 * h8 + 4);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int r = 8 * h8 + i;
+            const int off = 32 * kb + 16 * h8 + i;
+            bool ok = off < lim_n && (off < lim_p || (off >= lo_w && off <= hi_w));
+            if (segb) ok = ok && (int)sg[i >> 2][i & 3] == seg_q;
+            const float t = pos ? s[kb][r] : s[kb][r] * a.c2;
+            s[kb][r] = ok ? t : kNegInf;
+          }
+        }
+      }
+      if (!pos) mul = 1.f;
+    } else if (need_mask) {
       // Key of element (kb, r) = kv0 + 8*hl + off with a constant off; it is
       // allowed iff off < lim (key < N, and key <= query under the causal mask).
       const int base = kv0 + 8 * hl;
@@ -368,13 +448,17 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
     };
     float lsum = 0.f;
     bool accepted = false;
-    if (j > 0) {
+    // The fast path needs a finite reference in every row: a row's reference
+    // stays -inf until a tile holds one of its allowed keys (the first tile
+    // always does, except under a general mask).
+    const bool fast = __all(m_run != kNegInf);
+    if (fast) {
       lsum = weights(m_run);
       accepted = __all(lsum <= kSumCap);
     }
     if (!accepted) {
-      // Row max of the scaled scores; key 0 is never masked, so it is finite
-      // on the first tile.
+      // Row max of the scaled scores (-inf for a row none of whose keys in this
+      // tile is allowed).
       float mx = s[0][0] * mul;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -382,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r] * mul);
       const float m_tile = max_pair32(mx);
       const bool need = m_tile > m_run + kTau;
-      if (j == 0 || __any(need)) {
+      if (!fast || __any(need)) {
         const float m_new = need ? m_tile : m_run;
         const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
         l_part *= alpha;
@@ -391,7 +475,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
         m_run = m_new;
-        lsum = weights(m_run);
+        // A row still without an allowed key has only -inf scores: any finite
+        // reference gives it zero weights.
+        lsum = weights(m_run == kNegInf ? 0.f : m_run);
       }
     }
     l_part += lsum;
@@ -417,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
       // Tile st has landed for every wave (tile st+1 may still be in flight),
       // and every LDS access of the previous step is complete.
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm_lds_barrier<2 * kLoads>();
+      wait_vm_lds_barrier<kTileLoads>();
       __builtin_amdgcn_sched_barrier(0);
       // The zeroed V^T slot read at st = 0 is visible only after this barrier.
       mfma_phase((st + kTSlots - 1) % kTSlots, st % kKSlots, copy_tile_of(st), (st + 2) % kKSlots, st > 0);
@@ -438,7 +524,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   } else {
     for (int st = 0; st <= nt; ++st) {
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm_lds_barrier<2 * kLoads>();
+      wait_vm_lds_barrier<kTileLoads>();
       __builtin_amdgcn_sched_barrier(0);
       if (st < nt) transpose_read(st);
       if (st >= 1 && wave_active(st - 1)) softmax(st - 1);

@@ -50,8 +50,34 @@ typedef enum {
   FA2_ERR_ALIGN = 6,   /* a pointer is not 16-byte aligned */
   FA2_ERR_ALIAS = 7,   /* an output overlaps an input or another output */
   FA2_ERR_DEVICE = 8,  /* no current HIP device, or it is not a gfx950 */
-  FA2_ERR_LAUNCH = 9   /* the HIP launch itself reported an error */
+  FA2_ERR_LAUNCH = 9,  /* the HIP launch itself reported an error */
+  FA2_ERR_MASK = 10    /* fa2_fwd_masked: a window bound below -1, a negative
+                          prefix, or segment ids not 4-byte aligned */
 } fa2_status;
+
+/*
+ * A general attention mask for fa2_fwd_masked.  Key c is visible to query r
+ * (both in [0, N)) iff
+ *   segment_ids == NULL or segment_ids[b*N + c] == segment_ids[b*N + r], and
+ *   c < prefix, or
+ *   (window_left  < 0 or c >= r - window_left) and
+ *   (window_right < 0 or c <= r + window_right)  [causal: window_right = 0].
+ * Every query sees at least itself, so no row is ever empty.
+ *  - A mask is a 0 / -inf term added to the scores before the softmax, and the
+ *    same block-skipping scheme as the causal mask covers sliding windows,
+ *    document boundaries and prefix language models: "Flash Attention 2",
+ *    section "Causal masking" (its option A).  Tiles no pair of which is
+ *    visible are not visited (window bounds), tiles only partly visible are
+ *    masked element by element.
+ */
+typedef struct {
+  int causal;                 /* nonzero: key <= query (sets window_right to 0) */
+  int64_t window_left;        /* -1: no left bound; else key >= query - window_left */
+  int64_t window_right;       /* -1: no right bound; else key <= query + window_right */
+  int64_t prefix;             /* keys < prefix are visible to every query of the same segment */
+  const int32_t* segment_ids; /* NULL, or a [B, N] device array of int32 document ids shared
+                                 by all heads (4-byte aligned); read only */
+} fa2_mask;
 
 /*
  * fa2_fwd -- enqueue the forward pass on `stream` and return without waiting.
@@ -85,6 +111,16 @@ typedef enum {
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             int64_t B, int64_t H, int64_t N, int64_t d,
             int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa2_fwd_masked -- fa2_fwd under a general mask (NULL: no mask).  Arguments,
+ * layout, ownership and errors as for fa2_fwd, plus FA2_ERR_MASK; segment_ids
+ * must not overlap o or lse.  fa2_fwd(..., causal, ...) is this call with
+ * {causal, -1, -1, 0, NULL}.
+ */
+int fa2_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t N, int64_t d,
+                   const fa2_mask* mask, float scale, int dtype, void* stream);
 
 /*
  * fa2_bwd -- enqueue the gradients of fa2_fwd on `stream` and return without
@@ -126,8 +162,8 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const vo
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char* fa2_status_str(int status);
 
-/* Last HIP error code seen by a failing fa2_fwd or fa2_bwd call on this thread
- * (0 if none); useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
+/* Last HIP error code seen by a failing fa2_fwd, fa2_fwd_masked or fa2_bwd call
+ * on this thread (0 if none); useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
 int fa2_last_hip_error(void);
 
 #ifdef __cplusplus

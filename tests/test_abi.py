@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 10):
+    for code in range(0, 11):
         s = fa.fa2_status_str(code)
         assert s and s != "unknown status"
     assert fa.fa2_status_str(123) == "unknown status"
@@ -166,3 +166,35 @@ def test_python_backward_rejects_bad_tensors(lib):
         fa.backward(q, q, q, q, q[:, :, :4], lse)
     with pytest.raises(TypeError):
         fa.backward(q, q, q, q, q.float(), lse)
+
+
+# --- fa2_fwd_masked ----------------------------------------------------------------
+
+def _masked(mask, B=1, H=1, N=16, d=64, scale=0.125, dtype=0, o=O, lse=L):
+    return fa.fa2_fwd_masked(Q, K, V, o, lse, B, H, N, d, mask, scale, dtype, None)
+
+
+@pytest.mark.parametrize("fields,code", [
+    (dict(window_left=-2), fa.FA2_ERR_MASK), (dict(window_right=-5), fa.FA2_ERR_MASK),
+    (dict(prefix=-1), fa.FA2_ERR_MASK), (dict(segment_ids=0x60000002), fa.FA2_ERR_MASK),
+    (dict(segment_ids=O + 64), fa.FA2_ERR_ALIAS), (dict(segment_ids=L), fa.FA2_ERR_ALIAS),
+])
+def test_masked_argument_checks(lib, fields, code):
+    m = fa.Fa2Mask(0, -1, -1, 0, None)
+    for k_, v_ in fields.items():
+        setattr(m, k_, v_)
+    assert _masked(m) == code
+
+
+def test_masked_empty_problem_and_null_mask(lib):
+    assert _masked(fa.Fa2Mask(1, 3, 0, 2, None), B=0) == fa.FA2_OK
+    assert _masked(None, N=0) == fa.FA2_OK
+
+
+def test_masked_valid_call_without_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    for mask in (None, fa.Fa2Mask(1, 5, 0, 3, 0x60000000), fa.Fa2Mask(0, -1, -1, 0, None)):
+        for d in (64, 128, 256):
+            assert _masked(mask, d=d, N=333) == fa.FA2_ERR_DEVICE

@@ -449,9 +449,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
     float lsum = 0.f;
     bool accepted = false;
     // The fast path needs a finite reference in every row: a row's reference
-    // stays -inf until a tile holds one of its allowed keys (the first tile
-    // always does, except under a general mask).
-    const bool fast = __all(m_run != kNegInf);
+    // stays -inf until a tile holds one of its allowed keys.  Without a general
+    // mask the first tile always does (key 0 is visible to every row).
+    const bool fast = kGeneral ? __all(m_run != kNegInf) : step > 0;
     if (fast) {
       lsum = weights(m_run);
       accepted = __all(lsum <= kSumCap);
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
         m_run = m_new;
         // A row still without an allowed key has only -inf scores: any finite
         // reference gives it zero weights.
-        lsum = weights(m_run == kNegInf ? 0.f : m_run);
+        lsum = weights(kGeneral && m_run == kNegInf ? 0.f : m_run);
       }
     }
     l_part += lsum;

@@ -47,6 +47,29 @@ def flop_count(B: int, H: int, N: int, d: int, causal: bool) -> float:
     return f / 2.0 if causal else f
 
 
+def visible_pairs(N: int, causal: bool, window=None, prefix: int = 0, doc_len: int = 0) -> float:
+    """Number of (query, key) pairs a general mask leaves visible: the window
+    [r - wl, r + wr] (causal: wr = 0) and the prefix [0, prefix), each cut to
+    the row's document when contiguous documents of doc_len rows are given."""
+    import numpy as np
+
+    wl, wr = window if window is not None else (-1, -1)
+    if causal:
+        wr = 0
+    r = np.arange(N, dtype=np.int64)
+    ds = (r // doc_len) * doc_len if doc_len else np.zeros(N, dtype=np.int64)
+    de = np.minimum(ds + doc_len, N) - 1 if doc_len else np.full(N, N - 1, dtype=np.int64)
+    lo = np.maximum(ds, r - wl) if wl >= 0 else ds
+    hi = np.minimum(de, r + wr) if wr >= 0 else de
+    pl, ph = ds, np.minimum(de, prefix - 1)
+
+    def size(a, b):
+        return np.maximum(0, b - a + 1)
+
+    both = size(np.maximum(lo, pl), np.minimum(hi, ph))
+    return float(np.sum(size(lo, hi) + size(pl, ph) - both))
+
+
 def kernel_source_digest(sources=None) -> str:
     h = hashlib.sha256()
     for p in sources or KERNEL_SOURCES:
@@ -171,6 +194,11 @@ def main() -> int:
     ap.add_argument("--min-warmup-ms", type=float, default=300.0,
                     help="extra untimed steps until the warm-up has lasted this long (clock ramp-up)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--window", type=int, nargs=2, default=None, metavar=("LEFT", "RIGHT"),
+                    help="forward pass under a sliding window (-1: no bound on that side)")
+    ap.add_argument("--prefix", type=int, default=0, help="forward pass: keys below this are visible to every query")
+    ap.add_argument("--documents", type=int, default=0,
+                    help="forward pass: split each sequence into this many equal contiguous documents")
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward pass (the headline) or the gradient pass of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
@@ -200,6 +228,10 @@ def main() -> int:
         log(f"copied {n} bytes 5 times")
         return 0
 
+    if args.pass_ == "bwd" and (args.window is not None or args.prefix > 0 or args.documents > 0):
+        log("the gradient pass supports the causal mask and no mask only")
+        return 2
+
     import exact_attention_11_amd as fa
     from exact_attention_11_amd.inputs import WORKLOADS, workload_inputs
 
@@ -211,7 +243,24 @@ def main() -> int:
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    if args.pass_ == "fwd":
+    masked = args.window is not None or args.prefix > 0 or args.documents > 0
+    mask_cfg = None
+    if args.pass_ == "fwd" and masked:
+        doc_len = -(-w.N // args.documents) if args.documents > 0 else 0
+        seg = None
+        if doc_len:
+            seg = (torch.arange(w.N, dtype=torch.int32) // doc_len).repeat(w.B, 1).contiguous().cuda()
+        window = tuple(args.window) if args.window is not None else None
+
+        def step():
+            fa.forward(dq, dk, dv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream, window=window,
+                       prefix=args.prefix, segment_ids=seg)
+        pairs = visible_pairs(w.N, w.causal, window, args.prefix, doc_len)
+        flop = 4.0 * w.B * w.H * w.d * pairs
+        mask_cfg = {"window": list(window) if window else None, "prefix": args.prefix, "documents": args.documents,
+                    "visible_pairs_per_head": pairs}
+        metric = "attention fwd TFLOP/s over visible pairs (general mask), % of MI355X FP16/BF16 MFMA peak"
+    elif args.pass_ == "fwd":
         def step():
             fa.forward(dq, dk, dv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
         flop = flop_count(w.B, w.H, w.N, w.d, w.causal)
@@ -267,7 +316,7 @@ def main() -> int:
     log(f"{args.steps} steps: {ms_per_step:.4f} ms/step (events), launch avg {avg_launch_ms:.4f} ms, "
         f"min {min(launch_ms):.4f} ms, wall {wall_s * 1e3 / args.steps:.4f} ms/step -> {value:.1f} TFLOP/s")
 
-    traffic = recorded_traffic(w.name) if args.pass_ == "fwd" else None
+    traffic = recorded_traffic(w.name) if args.pass_ == "fwd" and not masked else None
     result = {
         "metric": metric,
         "value": round(value, 3),
@@ -283,7 +332,7 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "pass": args.pass_, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "inputs": w.dist, "flop_per_step": flop,
+                   "causal": w.causal, "mask": mask_cfg, "inputs": w.dist, "flop_per_step": flop,
                    "kernel_source_digest": kernel_source_digest(
                        KERNEL_SOURCES if args.pass_ == "fwd" else BWD_KERNEL_SOURCES)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_MFMA_TFLOPS,
@@ -293,7 +342,9 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the workload ...")
-        if args.pass_ == "fwd":
+        if args.pass_ == "fwd" and masked:
+            result["cpu_baseline"] = None  # the row-sampled oracle covers the plain masks only
+        elif args.pass_ == "fwd":
             result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
         else:
             result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, dout_h, args.cpu_seconds)

@@ -71,7 +71,8 @@ hipError_t launch_m(const fa2::FwdArgs& args, int mask_mode, hipStream_t stream)
   switch (mask_mode) {
     case fa2::kMaskNone: return launch<kDType, D, fa2::kMaskNone>(args, stream);
     case fa2::kMaskCausal: return launch<kDType, D, fa2::kMaskCausal>(args, stream);
-    default: return launch<kDType, D, fa2::kMaskGeneral>(args, stream);
+    case fa2::kMaskGeneral: return launch<kDType, D, fa2::kMaskGeneral>(args, stream);
+    default: return launch<kDType, D, fa2::kMaskSegments>(args, stream);
   }
 }
 
@@ -149,9 +150,10 @@ int fa2_fwd_masked(const void* q, const void* k, const void* v, void* o, float* 
   if (m.window_left < -1 || m.window_right < -1 || m.prefix < 0) return FA2_ERR_MASK;
   if (((uintptr_t)m.segment_ids) & 3) return FA2_ERR_MASK;
   if (B == 0 || H == 0 || N == 0) return FA2_OK;  // empty problem: nothing to do
-  // Index limits: rows fit in int32 inside the kernel, the grid in 2^31 - 1
-  // workgroups, byte sizes in 63 bits.
-  if (N > (int64_t)INT32_MAX - 256) return FA2_ERR_SHAPE;
+  // Index limits: rows (plus the span of one pass of the segment-id scan) fit
+  // in int32 inside the kernel, the grid in 2^31 - 1 workgroups, byte sizes in
+  // 63 bits.
+  if (N > (int64_t)INT32_MAX - 65536) return FA2_ERR_SHAPE;
   if (B > INT32_MAX || H > INT32_MAX) return FA2_ERR_SHAPE;
   const int64_t bh = B * H;  // both < 2^31: no overflow
   const int64_t br = rows_per_workgroup(d);
@@ -185,7 +187,7 @@ int fa2_fwd_masked(const void* q, const void* k, const void* v, void* o, float* 
     prefix = 0;
   }
   if (wl < 0 && wr < 0) prefix = 0;  // the window admits every key already
-  int mode = fa2::kMaskGeneral;
+  int mode = m.segment_ids ? fa2::kMaskSegments : fa2::kMaskGeneral;
   if (!m.segment_ids && prefix == 0 && wl < 0) {
     if (wr < 0) mode = fa2::kMaskNone;
     else if (wr == 0) mode = fa2::kMaskCausal;
@@ -210,6 +212,7 @@ int fa2_fwd_masked(const void* q, const void* k, const void* v, void* o, float* 
   args.prefix = (int)prefix;
   args.H = (int)H;
   args.seg = m.segment_ids;
+  args.grow = mode == fa2::kMaskGeneral && wl < 0 && wr >= 0;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_d<0>(args, d, mode, s) : launch_d<1>(args, d, mode, s);

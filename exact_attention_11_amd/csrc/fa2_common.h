@@ -38,20 +38,23 @@ struct FwdArgs {
   int n_qtiles;  // ceil(N / query rows per workgroup)
   int n_wg;      // B * H * n_qtiles
   float c2;      // scale * log2(e)
-  // General mask (used by the kMaskGeneral instances only): key c is visible
-  // to query r iff c < N, seg[b, c] == seg[b, r] (when seg is given), and
-  // c < prefix or r - wl <= c <= r + wr (a negative bound is no bound).
+  // General mask (used by the kMaskGeneral and kMaskSegments instances only):
+  // key c is visible to query r iff c < N, seg[b, c] == seg[b, r] (segment
+  // instances), and c < prefix or r - wl <= c <= r + wr (a negative bound is
+  // no bound).
   int wl;
   int wr;
   int prefix;
   int H;            // heads per batch: batch b = (b*H + h) / H
   const int* seg;   // [B, N] segment ids, or nullptr
+  int grow;         // general mask whose tile cost grows with the query tile (order those heaviest first)
 };
 
 // Mask modes of the forward kernels.
 constexpr int kMaskNone = 0;
 constexpr int kMaskCausal = 1;
-constexpr int kMaskGeneral = 2;
+constexpr int kMaskGeneral = 2;   // window and prefix
+constexpr int kMaskSegments = 3;  // window, prefix and segment ids
 
 // Element-type specific pieces: the MFMA and the fp32 -> storage conversion.
 template <int kDType> struct Elem;
@@ -140,6 +143,119 @@ __device__ __forceinline__ float sum_pair32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wave-wide minimum and maximum (every lane receives the result).
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = min(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = max(x, __shfl_xor(x, m));
+  return x;
+}
+
+// Key tiles (of bc keys) that a general mask leaves to the query rows q0..q1,
+// as at most two runs of consecutive tiles: the prefix, then the window around
+// the rows (one run when the two meet).  Step s of the key loop visits tile
+// a0 + s for s < na, else b0 + s - na.  Both runs are cut to the keys kf..kl
+// (the keys whose segment ids can match those of the rows; 0..N-1 without
+// segment ids).  Row q0 always sees key q0, so na + nb >= 1.
+struct TileRuns {
+  int a0, na, b0, nb;
+};
+__device__ __forceinline__ TileRuns general_runs(const FwdArgs& a, int q0, int q1, int kf, int kl, int bc) {
+  const int N = a.N;
+  const int w_lo = a.wl < 0 ? 0 : max(0, q0 - a.wl);
+  const int w_hi = a.wr < 0 ? N - 1 : min(N - 1, q1 + a.wr);
+  int b0 = w_lo / bc, b1 = w_hi / bc + 1;          // window tiles [b0, b1)
+  int a0 = 0, a1 = (min(a.prefix, N) + bc - 1) / bc;  // prefix tiles [0, a1)
+  if (a1 >= b0) {  // the runs touch: one run
+    b0 = 0;
+    b1 = max(a1, b1);
+    a1 = 0;
+  }
+  const int f = kf / bc, l = kl / bc + 1;
+  a0 = max(a0, f);
+  a1 = min(a1, l);
+  b0 = max(b0, f);
+  b1 = min(b1, l);
+  TileRuns r;
+  r.a0 = a0;
+  r.na = max(0, a1 - a0);
+  r.b0 = b0;
+  r.nb = max(0, b1 - b0);
+  return r;
+}
+
+// Under segment ids: the first and last key in lo..hi whose id lies between the
+// least and the greatest id of the rows q0..q1 (kf, kl).  Every key that one of
+// those rows may see lies in kf..kl (and with ids that never decrease along the
+// sequence, documents, the bound is tight).  The rows' own keys match, so only
+// lo..q0-1 and q1+1..hi are read (q0..q1 must lie in lo..hi).  All threads of
+// the workgroup take part; red holds 2 ints per wave.  The row ids and the first
+// batch of key ids are all in flight at once, so a span of up to
+// kUnroll * 64 * kWaves keys costs one round trip to L2.
+template <int kWaves>
+__device__ void segment_span(const int* __restrict__ segb, int q0, int q1, int lo, int hi, FA2_LDS int* red,
+                             int& kf, int& kl) {
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kRowLoads = (32 * kWaves + 63) / 64;  // rows q0..q1 over the 64 lanes of each wave
+  constexpr int kUnroll = 32;                         // key loads in flight per lane
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = q0 - lo, n = nl + (hi - q1);  // keys left of the rows, then right of them
+  int rv[kRowLoads];
+#pragma unroll
+  for (int u = 0; u < kRowLoads; ++u) rv[u] = segb[min(q0 + lane + 64 * u, q1)];
+  int kv[kUnroll];
+  auto load_batch = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = base + u * kThreads + tid;
+      const int c = i >= n ? q0 : (i < nl ? lo + i : q1 + 1 + (i - nl));
+      kv[u] = segb[c];
+    }
+  };
+  load_batch(0);
+  int qmin = rv[0], qmax = rv[0];
+#pragma unroll
+  for (int u = 1; u < kRowLoads; ++u) {
+    qmin = min(qmin, rv[u]);
+    qmax = max(qmax, rv[u]);
+  }
+  qmin = wave_min(qmin);
+  qmax = wave_max(qmax);
+  int f = q0, l = q1;
+  for (int base = 0;;) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = base + u * kThreads + tid;
+      const int c = i < nl ? lo + i : q1 + 1 + (i - nl);
+      if (i < n && kv[u] >= qmin && kv[u] <= qmax) {
+        f = min(f, c);
+        l = max(l, c);
+      }
+    }
+    base += kUnroll * kThreads;
+    if (base >= n) break;
+    load_batch(base);
+  }
+  f = wave_min(f);
+  l = wave_max(l);
+  if (lane == 0) {
+    red[2 * wave] = f;
+    red[2 * wave + 1] = l;
+  }
+  __syncthreads();
+  kf = red[0];
+  kl = red[1];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    kf = min(kf, red[2 * w]);
+    kl = max(kl, red[2 * w + 1]);
+  }
+}
+
 // Workgroup id -> (head, query tile).  Consecutive dispatch ids go round-robin
 // over the 8 XCDs (32 CUs and one L2 each on MI355X), so id w runs on XCD w % 8.
 //  * Without a mask every tile costs the same: regroup the ids so that each XCD
@@ -152,6 +268,8 @@ __device__ __forceinline__ float sum_pair32(float x) {
 //    fills about one round of the XCD's CUs, which keeps the concurrent
 //    workgroups on few heads (L2 reuse) while every CU's queue still runs
 //    heaviest first.  Otherwise all heads' heaviest tiles go first.
+//    General masks whose cost grows with the row (a right bound and no left
+//    bound) are ordered the same way.
 constexpr int kCusPerXcd = 32;
 __device__ __forceinline__ void wg_to_tile(const FwdArgs& a, bool causal, int& bh, int& qtile) {
   const int w = blockIdx.x;

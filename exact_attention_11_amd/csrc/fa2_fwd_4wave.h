@@ -70,7 +70,8 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src_head,
 template <int kDType, int D, int kMask>
 __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdArgs a) {
   constexpr bool kCausal = kMask == kMaskCausal;
-  constexpr bool kGeneral = kMask == kMaskGeneral;
+  constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
+  constexpr bool kSeg = kMask == kMaskSegments;
   typedef Elem<kDType> E;
   typedef typename E::V8 V8;
   constexpr int CPR = D / 8;
@@ -83,10 +84,17 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   __shared__ __attribute__((aligned(1024))) uint16_t sV_[kBc * D];
   FA2_LDS uint16_t* const sK = (FA2_LDS uint16_t*)sK_;
   FA2_LDS uint16_t* const sV = (FA2_LDS uint16_t*)sV_;
+  __shared__ int red_[kSeg ? 2 * kWaves : 2];
+  // Segment ids of the keys of the current and of the next K tile.
+  __shared__ __attribute__((aligned(16))) int seg_[kSeg ? 2 * kBc : 4];
+  FA2_LDS int* const sSeg = (FA2_LDS int*)seg_;
+  // Copies in flight per wave for one K tile: its rows, plus under segment ids
+  // the keys' ids (copied by every wave, so the counts stay uniform).
+  constexpr int kKLoads = kLoads + (kSeg ? 1 : 0);
 
   const int N = a.N;
   int bh, qtile;
-  wg_to_tile(a, kCausal, bh, qtile);
+  wg_to_tile(a, kCausal || (kGeneral && a.grow), bh, qtile);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -99,31 +107,53 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   const uint16_t* __restrict__ kh = a.k + head_off;
   const uint16_t* __restrict__ vh = a.v + head_off;
 
-  // Key tiles t0 .. t_end - 1 are visited.
-  int t0 = 0, t_end;
-  if constexpr (kGeneral) {
-    const int q0 = qtile * kBr, q1 = min(N, q0 + kBr) - 1;
-    // Last visible key: the window's right edge, or the prefix's end if later.
-    const int hi = a.wr < 0 ? N - 1 : min(N - 1, max(q1 + a.wr, a.prefix - 1));
-    const int lo = (a.prefix > 0 || a.wl < 0) ? 0 : max(0, q0 - a.wl);
-    t0 = lo / kBc;
-    t_end = hi / kBc + 1;
-  } else {
-    const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
-    t_end = (kv_end + kBc - 1) / kBc;
-  }
+  // Key tiles: step st of the loop visits tile tile_of(st), st < nt (as in the
+  // eight-wave kernel: tiles 0 .. nt-1 without a general mask, the runs of
+  // general_runs with one).
+  int nt, run_a0 = 0, run_na = 0, run_b0 = 0;
   const int* __restrict__ segb = nullptr;  // this batch's segment ids
   int seg_q = 0;
   if constexpr (kGeneral) {
-    if (a.seg) {
+    const int q0 = qtile * kBr, q1 = min(N, q0 + kBr) - 1;
+    int kf = 0, kl = N - 1;
+    if constexpr (kSeg) {
       segb = a.seg + (int64_t)(bh / a.H) * N;
       seg_q = segb[min(my_q, N - 1)];
+      const TileRuns all = general_runs(a, q0, q1, 0, N - 1, kBc);
+      const int lo = all.na > 0 ? 0 : all.b0 * kBc;
+      const int hi = min(N - 1, (all.b0 + all.nb) * kBc - 1);
+      segment_span<kWaves>(segb, q0, q1, lo, hi, (FA2_LDS int*)red_, kf, kl);
     }
+    const TileRuns r = general_runs(a, q0, q1, kf, kl, kBc);
+    run_a0 = r.a0;
+    run_na = r.na;
+    run_b0 = r.b0;
+    nt = r.na + r.nb;
+  } else {
+    const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
+    nt = (kv_end + kBc - 1) / kBc;
+  }
+  auto tile_of = [&](int step) __attribute__((always_inline)) {
+    if constexpr (kGeneral) return step < run_na ? run_a0 + step : run_b0 + (step - run_na);
+    else return step;
+  };
+  // With segment ids: when all 32 rows of this wave share one id (seg_w), a
+  // tile's class follows from a comparison of each key's id with it.
+  bool rows_one_seg = false;
+  int seg_w = 0;
+  if constexpr (kSeg) {
+    seg_w = __builtin_amdgcn_readfirstlane(seg_q);
+    rows_one_seg = __all(seg_q == seg_w);
   }
 
+  auto load_k = [&](int kv0, int st) __attribute__((always_inline)) {
+    load_tile<D, false>(kh, sK, kv0, N, wave, lane);
+    if constexpr (kSeg) dma4(segb + min(kv0 + lane, N - 1), sSeg + (st & 1) * kBc);
+  };
+
   // First K and V tiles start streaming before anything else.
-  load_tile<D, false>(kh, sK, t0 * kBc, N, wave, lane);
-  load_tile<D, true>(vh, sV, t0 * kBc, N, wave, lane);
+  load_k(tile_of(0) * kBc, 0);
+  load_tile<D, true>(vh, sV, tile_of(0) * kBc, N, wave, lane);
 
   // Q fragments (B operand of S^T = K Q^T), loaded once and kept in registers.
   // They are consumed right here so that the compiler's own wait for them
@@ -143,18 +173,17 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   float m_run = kNegInf;  // reference max of this lane's query row (log2 units)
   float l_part = 0.f;     // this lane's share of the row sum
 
-  for (int j = t0; j < t_end; ++j) {
-    const int kv0 = j * kBc;
+  for (int st = 0; st < nt; ++st) {
+    const int kv0 = tile_of(st) * kBc;
     // Wave-uniform classification of this tile for this wave's 32 rows.
     bool active = !kCausal || kv0 <= q_row0 + 31;
     bool need_mask = (kv0 + kBc > N) || (kCausal && kv0 + kBc - 1 > q_row0);
     if constexpr (kGeneral) {
       const int k1 = kv0 + kBc - 1, qa = q_row0, qb = q_row0 + 31;
       active = !(kv0 >= a.prefix && ((a.wr >= 0 && kv0 > qb + a.wr) || (a.wl >= 0 && k1 < qa - a.wl)));
-      need_mask = !(k1 < N && !segb &&
+      need_mask = !(k1 < N &&
                     (k1 < a.prefix || ((a.wl < 0 || kv0 >= qb - a.wl) && (a.wr < 0 || k1 <= qa + a.wr))));
     }
-    const bool generic = need_mask || !(a.c2 > 0.f);
 
     wait_vm_barrier<kLoads>();  // K_j has landed (V_j may still be in flight)
     f32x16 s[2];
@@ -175,8 +204,22 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
     // The prefetch is issued on every step (the last step re-reads its own
     // tile, which nobody consumes) so that the number of loads in flight is the
     // same on every path through the loop.
-    const int kv_next = j + 1 < t_end ? kv0 + kBc : kv0;
-    load_tile<D, false>(kh, sK, kv_next, N, wave, lane);
+    const int kv_next = st + 1 < nt ? tile_of(st + 1) * kBc : kv0;
+    load_k(kv_next, st + 1);
+
+    // Under segment ids: no key of the tile shares the rows' one id (nothing
+    // survives), or every key does (the ids need no comparison).
+    bool seg_all = false;
+    const FA2_LDS int* sk = sSeg + (st & 1) * kBc;
+    if constexpr (kSeg) {
+      if (rows_one_seg) {
+        const int seg_k = sk[lane];
+        seg_all = __all(seg_k == seg_w);
+        active = active && __any(seg_k == seg_w);
+      }
+      if (!seg_all) need_mask = true;
+    }
+    const bool generic = need_mask || !(a.c2 > 0.f);
 
     uint32_t pk[2][8];  // probabilities, packed pairs, B-operand order
     if (active) {
@@ -185,6 +228,11 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
         // Scale first, then mask: t = -inf for keys past N or after the query.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+          u32x4 sg[4] = {};
+          if (kSeg && !seg_all) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) sg[g4] = *(const FA2_LDS u32x4*)(sk + 32 * kb + 8 * g4 + 4 * hl);
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
@@ -192,7 +240,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
             if constexpr (kGeneral) {
               masked = key >= N ||
                        !(key < a.prefix || ((a.wl < 0 || key >= my_q - a.wl) && (a.wr < 0 || key <= my_q + a.wr)));
-              if (segb) masked = masked || segb[min(key, N - 1)] != seg_q;
+              if (kSeg && !seg_all) masked = masked || (int)sg[r >> 2][r & 3] != seg_q;
             }
             const float t = s[kb][r] * a.c2;
             s[kb][r] = masked ? kNegInf : t;
@@ -233,7 +281,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
       l_part += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
 
-    wait_vm_barrier<kLoads>();  // V_j has landed (K_{j+1} may be in flight)
+    wait_vm_barrier<kKLoads>();  // V_j has landed (K_{j+1} may be in flight)
     if (active) {
       const int g = lane >> 4;
       const int L = lane & 15;

@@ -88,7 +88,8 @@ template <int CPR> __device__ __forceinline__ uint32_t vs_byte(int row, int chun
 template <int kDType, int D, int kMask>
 __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   constexpr bool kCausal = kMask == kMaskCausal;
-  constexpr bool kGeneral = kMask == kMaskGeneral;
+  constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
+  constexpr bool kSeg = kMask == kMaskSegments;
   typedef Elem<kDType> E;
   typedef typename E::V8 V8;
   constexpr int CPR = D / 8;                          // 16-byte chunks per K/V row
@@ -101,20 +102,21 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(kLoads >= 1 && kLoads * 64 * kWaves == kBc * CPR, "tile copy split");
   // Copy instructions per wave per tile: K and V, plus the keys' segment ids
-  // under a general mask (issued by every wave, so the counts stay uniform).
-  constexpr int kTileLoads = 2 * kLoads + (kGeneral ? 1 : 0);
+  // under segment ids (issued by every wave, so the counts stay uniform).
+  constexpr int kTileLoads = 2 * kLoads + (kSeg ? 1 : 0);
   constexpr int kSegSlots = 4;  // segment ids of tiles st..st+2 stay readable while group 1 reads st-1
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem_[(kKSlots + kVSlots + kTSlots) * kTile];
   FA2_LDS uint16_t* const sK = (FA2_LDS uint16_t*)smem_;
   FA2_LDS uint16_t* const sVs = sK + kKSlots * kTile;
   FA2_LDS uint16_t* const sVt = sVs + kVSlots * kTile;
-  __shared__ __attribute__((aligned(16))) int seg_[kGeneral ? kSegSlots * kBc : 4];
+  __shared__ __attribute__((aligned(16))) int seg_[kSeg ? kSegSlots * kBc : 4];
   FA2_LDS int* const sSeg = (FA2_LDS int*)seg_;
+  __shared__ int red_[kSeg ? 2 * kWaves : 2];
 
   const int N = a.N;
   int bh, qtile;
-  wg_to_tile(a, kCausal, bh, qtile);
+  wg_to_tile(a, kCausal || (kGeneral && a.grow), bh, qtile);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -141,36 +143,51 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   const uint32_t voffK = (uint32_t)((sigma(kr) * D + cch * 8) * 2);
   const uint32_t voffV = (uint32_t)((vr * D + cch * 8) * 2);
 
-  // Key tiles t0 .. t0 + nt - 1 are visited (step st handles tile t0 + st).
-  int t0 = 0, t_end;
-  if constexpr (kGeneral) {
-    const int q0 = qtile * kBr, q1 = min(N, q0 + kBr) - 1;
-    // Last visible key: the window's right edge, or the prefix's end if later.
-    const int hi = a.wr < 0 ? N - 1 : min(N - 1, max(q1 + a.wr, a.prefix - 1));
-    const int lo = (a.prefix > 0 || a.wl < 0) ? 0 : max(0, q0 - a.wl);
-    t0 = lo / kBc;
-    t_end = hi / kBc + 1;
-  } else {
-    const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
-    t_end = (kv_end + kBc - 1) / kBc;
-  }
-  const int nt = t_end - t0;
+  // Key tiles: step st of the loop visits tile tile_of(st), st < nt.  Without a
+  // general mask those are tiles 0 .. nt-1 (under the causal mask up to the
+  // rows' last key); a general mask visits the runs of general_runs, cut to the
+  // keys whose segment ids can match.
+  int nt, run_a0 = 0, run_na = 0, run_b0 = 0;
   const int* __restrict__ segb = nullptr;  // this batch's segment ids
   int seg_q = 0;                           // this lane's query's segment id
   if constexpr (kGeneral) {
-    if (a.seg) {
+    const int q0 = qtile * kBr, q1 = min(N, q0 + kBr) - 1;
+    int kf = 0, kl = N - 1;
+    if constexpr (kSeg) {
       segb = a.seg + (int64_t)(bh / a.H) * N;
       seg_q = segb[min(my_q, N - 1)];
+      const TileRuns all = general_runs(a, q0, q1, 0, N - 1, kBc);
+      const int lo = all.na > 0 ? 0 : all.b0 * kBc;
+      const int hi = min(N - 1, (all.b0 + all.nb) * kBc - 1);
+      segment_span<kWaves>(segb, q0, q1, lo, hi, (FA2_LDS int*)red_, kf, kl);
     }
+    const TileRuns r = general_runs(a, q0, q1, kf, kl, kBc);
+    run_a0 = r.a0;
+    run_na = r.na;
+    run_b0 = r.b0;
+    nt = r.na + r.nb;
+  } else {
+    const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
+    nt = (kv_end + kBc - 1) / kBc;
+  }
+  auto tile_of = [&](int step) __attribute__((always_inline)) {
+    if constexpr (kGeneral) return step < run_na ? run_a0 + step : run_b0 + (step - run_na);
+    else return step;
+  };
+  // With segment ids: when all 32 rows of this wave share one id (seg_w), a
+  // tile's class follows from a comparison of each key's id with it.
+  bool rows_one_seg = false;
+  int seg_w = 0;
+  if constexpr (kSeg) {
+    seg_w = __builtin_amdgcn_readfirstlane(seg_q);
+    rows_one_seg = __all(seg_q == seg_w);
   }
 
   auto issue_tile = [&](int step, int slot) __attribute__((always_inline)) {
-    const int kv0 = (t0 + step) * kBc;
-    if constexpr (kGeneral) {
-      // Segment ids of the tile's keys (every wave copies the same 256 bytes;
-      // without segment ids the copy reads K and is never used).
-      const void* src = segb ? (const void*)(segb + min(kv0 + lane, N - 1)) : (const void*)kh;
-      dma4(src, sSeg + (step % kSegSlots) * kBc);
+    const int kv0 = tile_of(step) * kBc;
+    if constexpr (kSeg) {
+      // Segment ids of the tile's keys (every wave copies the same 256 bytes).
+      dma4(segb + min(kv0 + lane, N - 1), sSeg + (step % kSegSlots) * kBc);
     }
     FA2_LDS uint16_t* dk = sK + slot * kTile;
     FA2_LDS uint16_t* dv = sVs + slot * kTile;
@@ -227,12 +244,22 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   uint32_t pk[2][8];      // probabilities of one tile, between softmax and P.V
 
   // Tile classes for this wave's 32 rows: does any (row, key) pair survive the
-  // mask, and does every pair?
+  // mask (wave_active), and does every pair (softmax's need_mask)?  Under
+  // segment ids wave_active also records whether every key of the tile shares
+  // the rows' one id (seg_all), for softmax on the same step.
+  bool seg_all = false;
   auto wave_active = [&](int step) __attribute__((always_inline)) {
-    const int k0 = (t0 + step) * kBc;
+    const int k0 = tile_of(step) * kBc;
     if constexpr (kGeneral) {
       const int qa = q_row0, qb = q_row0 + 31;
-      return !(k0 >= a.prefix && ((a.wr >= 0 && k0 > qb + a.wr) || (a.wl >= 0 && k0 + kBc - 1 < qa - a.wl)));
+      bool act = !(k0 >= a.prefix && ((a.wr >= 0 && k0 > qb + a.wr) || (a.wl >= 0 && k0 + kBc - 1 < qa - a.wl)));
+      seg_all = false;
+      if (kSeg && rows_one_seg) {
+        const int sk = sSeg[(step % kSegSlots) * kBc + lane];
+        seg_all = __all(sk == seg_w);
+        act = act && __any(sk == seg_w);
+      }
+      return act;
     } else {
       return !kCausal || k0 <= q_row0 + 31;
     }
@@ -363,11 +390,11 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   // whether the reference moves, O and l are rescaled by 2^(old - new), and the
   // weights are formed again.
   auto softmax = [&](int step) __attribute__((always_inline)) {
-    const int kv0 = (t0 + step) * kBc;
+    const int kv0 = tile_of(step) * kBc;
     bool need_mask = (kv0 + kBc > N) || (kCausal && kv0 + kBc - 1 > q_row0);
     if constexpr (kGeneral) {
       const int k1 = kv0 + kBc - 1, qa = q_row0, qb = q_row0 + 31;
-      const bool full = k1 < N && !segb &&
+      const bool full = k1 < N && (!kSeg || seg_all) &&
                         (k1 < a.prefix || ((a.wl < 0 || kv0 >= qb - a.wl) && (a.wr < 0 || k1 <= qa + a.wr)));
       need_mask = !full;
     }
@@ -386,7 +413,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
 #pragma unroll
         for (int h8 = 0; h8 < 2; ++h8) {
           u32x4 sg[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
-          if (segb) {
+          if (kSeg && !seg_all) {
             sg[0] = *(const FA2_LDS u32x4*)(sk + 32 * kb + 16 * h8);
             sg[1] = *(const FA2_LDS u32x4*)(sk + 32 * kb + 16 * h8 + 4);
           }
@@ -395,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
             const int r = 8 * h8 + i;
             const int off = 32 * kb + 16 * h8 + i;
             bool ok = off < lim_n && (off < lim_p || (off >= lo_w && off <= hi_w));
-            if (segb) ok = ok && (int)sg[i >> 2][i & 3] == seg_q;
+            if (kSeg && !seg_all) ok = ok && (int)sg[i >> 2][i & 3] == seg_q;
             const float t = pos ? s[kb][r] : s[kb][r] * a.c2;
             s[kb][r] = ok ? t : kNegInf;
           }

@@ -35,23 +35,26 @@ def _gpu():
     fa.load_library()
 
 
-def _segments(B, N, kind, seed):
+def _segments(B, N, kind, seed, n_docs=4):
     rng = np.random.default_rng(seed)
     seg = np.zeros((B, N), dtype=np.int32)
     for b in range(B):
-        if kind == "documents":  # contiguous documents of random lengths
-            cuts = np.sort(rng.choice(np.arange(1, N), size=min(N - 1, 4), replace=False)) if N > 1 else []
-            seg[b] = np.searchsorted(cuts, np.arange(N), side="right")
+        cuts = np.sort(rng.choice(np.arange(1, N), size=min(N - 1, n_docs), replace=False)) if N > 1 else []
+        runs = np.searchsorted(cuts, np.arange(N), side="right")
+        if kind == "documents":  # contiguous documents of random lengths, ids increasing
+            seg[b] = runs
+        elif kind == "shuffled":  # contiguous runs whose ids go up and down and repeat
+            seg[b] = rng.integers(0, max(2, n_docs // 2), size=runs.max() + 1)[runs]
         else:  # interleaved ids
             seg[b] = rng.integers(0, 3, size=N)
     return seg
 
 
-def _case(B, H, N, d, dtype, window=None, prefix=0, seg_kind=None, causal=False, seed=0):
+def _case(B, H, N, d, dtype, window=None, prefix=0, seg_kind=None, causal=False, seed=0, n_docs=4):
     q, k, v = make_qkv(B, H, N, d, dtype, "normal", seed)
     v = v * 0.25
     scale = 1.0 / math.sqrt(d)
-    seg = _segments(B, N, seg_kind, seed) if seg_kind else None
+    seg = _segments(B, N, seg_kind, seed, n_docs) if seg_kind else None
     what = f"B={B} H={H} N={N} d={d} {dtype} window={window} prefix={prefix} seg={seg_kind} causal={causal}"
     _log(f"case {what}")
     seg_t = torch.from_numpy(seg).cuda() if seg is not None else None
@@ -111,6 +114,32 @@ def test_mask_bounds_that_cannot_bite():
     _case(1, 2, 200, 128, torch.float16, window=(199, 500), seed=6)
     _case(1, 2, 200, 128, torch.float16, prefix=200, causal=True, seed=6)
     _case(1, 2, 200, 64, torch.float16, window=(400, -1), causal=True, seed=6)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_mask_many_documents(d, causal):
+    """Long sequences of many documents: each query tile visits only the key
+    tiles of the documents its rows belong to (first with ids that increase
+    along the sequence, then with runs whose ids repeat out of order)."""
+    _case(2, 2, 1500, d, torch.float16, seg_kind="documents", causal=causal, seed=10, n_docs=12)
+    _case(1, 2, 1500, d, torch.bfloat16, seg_kind="shuffled", causal=causal, seed=11, n_docs=12)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_mask_documents_with_window_and_prefix(d):
+    """Documents under a causal sliding window plus a prefix: the key tiles come
+    in two runs (prefix, then window) cut to the rows' documents."""
+    _case(2, 2, 1800, d, torch.float16, window=(200, 0), prefix=70, seg_kind="documents", seed=12, n_docs=6)
+    _case(1, 2, 1800, d, torch.float16, window=(150, 40), prefix=130, seg_kind="shuffled", seed=13, n_docs=8)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_mask_prefix_far_from_window(d):
+    """A prefix and a window far apart: most key tiles between them are never
+    visited."""
+    _case(1, 2, 2500, d, torch.float16, window=(300, 0), prefix=100, seed=14)
+    _case(1, 2, 2500, d, torch.bfloat16, window=(64, 64), prefix=1, seed=15)
 
 
 def test_mask_long_sliding_window():

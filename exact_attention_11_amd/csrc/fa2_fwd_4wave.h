@@ -33,37 +33,51 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per K/V tile
 
-// XOR swizzles of the 16-byte chunk index inside a tile row.
-//  K: the A-operand read of one MFMA touches 32 rows at the same logical chunk;
-//     the swizzle spreads every 16 consecutive rows over 16 distinct 16-byte
-//     bank groups (rows of 128 bytes pair up, hence the shift for d = 64).
-//  V: a transposed read touches 4 consecutive rows x 64 bytes per half wave;
+// LDS tile layouts (head dim D = 256: 32 chunks of 16 bytes per row).
+//  K: 256-byte blocks, block (row / 16, chunk) at index (row / 16) * CPR + chunk
+//     holding one chunk of 16 consecutive rows.  The A-operand read of 16 lanes
+//     (16 rows, one chunk) covers one whole block, so it is free of bank
+//     conflicts, and each lane reads at one base address plus an immediate.
+//  V: row-major, the chunk index of row r XOR-swizzled by 4 * (r % 4): a
+//     transposed read touches 4 consecutive rows x 64 bytes per half wave, and
 //     the swizzle puts those 4 rows in 4 distinct 64-byte bank windows.
-template <int D> __device__ __forceinline__ int swz_k(int row) {
-  return D == 64 ? ((row >> 1) & 7) : (row & 15);
-}
-template <int D> __device__ __forceinline__ int swz_v(int row) {
-  return D == 64 ? (((row >> 1) & 1) << 2) : ((row & 3) << 2);
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
+
+// Issue the global -> LDS copy of one kBc x D K tile (rows kv0.., clamped to
+// N - 1).  Copy instruction t of a wave fills the 1 KB at q = t * kWaves + wave,
+// blocks 4q .. 4q + 3: lane i copies row 16 * ((4q + i / 16) / CPR) + i % 16 at
+// chunk (4q + i / 16) % CPR.
+template <int D>
+__device__ __forceinline__ void load_k_tile(const uint16_t* __restrict__ kh, FA2_LDS uint16_t* dst, int kv0, int N,
+                                            int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int kPerWave = kBc * CPR / (64 * kWaves);
+#pragma unroll
+  for (int t = 0; t < kPerWave; ++t) {
+    const int q = t * kWaves + wave;
+    const int b = 4 * q + (lane >> 4);
+    const int row = 16 * (b / CPR) + (lane & 15);
+    const int grow = min(kv0 + row, N - 1);
+    dma16(kh + (int64_t)grow * D + (b % CPR) * 8, dst + q * 512);
+  }
 }
 
-// Issue the global -> LDS copy of one kBc x D tile (rows kv0.., clamped to N-1).
-// Each instruction of a wave fills 64 consecutive 16-byte LDS slots; slot s
-// holds logical chunk (s % CPR) ^ swz(row) of row s / CPR.
-template <int D, bool kIsV>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src_head, FA2_LDS uint16_t* dst,
-                                          int kv0, int N, int wave, int lane) {
-  constexpr int CPR = D / 8;                        // 16-byte chunks per row
-  constexpr int kPerWave = kBc * CPR / (64 * kWaves);  // instructions per wave
+// The same for a V tile (row-major, swizzled): each instruction of a wave fills
+// 64 consecutive 16-byte LDS slots; slot s holds logical chunk
+// (s % CPR) ^ swz_v(row) of row s / CPR.
+template <int D>
+__device__ __forceinline__ void load_v_tile(const uint16_t* __restrict__ vh, FA2_LDS uint16_t* dst, int kv0, int N,
+                                            int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int kPerWave = kBc * CPR / (64 * kWaves);
 #pragma unroll
   for (int t = 0; t < kPerWave; ++t) {
     const int s0 = (t * kWaves + wave) * 64;
     const int s = s0 + lane;
     const int row = s / CPR;
-    const int chp = s % CPR;
-    const int ch = chp ^ (kIsV ? swz_v<D>(row) : swz_k<D>(row));
+    const int ch = (s % CPR) ^ swz_v(row);
     const int grow = min(kv0 + row, N - 1);
-    const uint16_t* g = src_head + (int64_t)grow * D + ch * 8;
-    dma16(g, dst + s0 * 8);
+    dma16(vh + (int64_t)grow * D + ch * 8, dst + s0 * 8);
   }
 }
 
@@ -79,6 +93,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   constexpr int DB = D / 32;  // 32-wide blocks of the output columns
   constexpr int kLoads = kBc * CPR / (64 * kWaves);
   constexpr float kNegInf = -__builtin_huge_valf();
+  static_assert(D == 256, "the four-wave kernel serves head dim 256");
 
   __shared__ __attribute__((aligned(1024))) uint16_t sK_[kBc * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV_[kBc * D];
@@ -147,13 +162,13 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   }
 
   auto load_k = [&](int kv0, int st) __attribute__((always_inline)) {
-    load_tile<D, false>(kh, sK, kv0, N, wave, lane);
+    load_k_tile<D>(kh, sK, kv0, N, wave, lane);
     if constexpr (kSeg) dma4(segb + min(kv0 + lane, N - 1), sSeg + (st & 1) * kBc);
   };
 
   // First K and V tiles start streaming before anything else.
   load_k(tile_of(0) * kBc, 0);
-  load_tile<D, true>(vh, sV, tile_of(0) * kBc, N, wave, lane);
+  load_v_tile<D>(vh, sV, tile_of(0) * kBc, N, wave, lane);
 
   // Q fragments (B operand of S^T = K Q^T), loaded once and kept in registers.
   // They are consumed right here so that the compiler's own wait for them
@@ -173,6 +188,45 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   float m_run = kNegInf;  // reference max of this lane's query row (log2 units)
   float l_part = 0.f;     // this lane's share of the row sum
 
+  // Operand reads run as pipelines kPipe fragments ahead of the MFMAs that use
+  // them; the scheduling fences keep the compiler from hoisting every read of a
+  // phase (a register quad each), which would spill.  Consecutive MFMAs use
+  // different accumulators.
+  constexpr int kPipe = 4;
+  V8 fr[kPipe];
+  // S^T = K Q^T, fragment f: key block kb = f % 2, k-step ks = f / 2; lane
+  // (hl, col) reads row 32 kb + col, chunk 2 ks + hl of the K tile.
+  const uint32_t kbase = opaque_vgpr((uint32_t)(size_t)sK + (uint32_t)(((((col >> 4) * CPR) + hl) << 8) + ((col & 15) << 4)));
+  auto k_frag = [&](int f) __attribute__((always_inline)) {
+    const uint32_t ad = kbase + (uint32_t)(((2 * (f & 1) * CPR) + 2 * (f >> 1)) << 8);
+    return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(size_t)ad);
+  };
+  // O^T += V^T P^T, fragment f: key block c = f / DB, output block db = f % DB.
+  // Lane (g, L) = (lane / 16, lane % 16) takes keys kr = 16 c + 4 (g / 2) + L / 4
+  // and kr + 8, columns 32 db + 16 (g % 2) + 4 (L % 4) .. + 3, from the
+  // swizzled V tile: chunk 4 db + y with y = 2 (g % 2) + (L % 4) / 2 lands at
+  // 4 (db ^ x) + y, x = kr % 4 = L / 4, so each lane keeps one base address per
+  // value of db % 4 and everything else is an immediate.
+  uint32_t vbase[4];
+  {
+    const int g = lane >> 4, L = lane & 15;
+    const int x = L >> 2, y = 2 * (g & 1) + ((L & 3) >> 1);
+    const uint32_t lane_part = (uint32_t)((4 * (g >> 1) + x) * CPR * 16 + 16 * y + 8 * (L & 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vbase[j] = opaque_vgpr((uint32_t)(size_t)sV + lane_part + (uint32_t)(64 * (j ^ x)));
+  }
+  auto v_frag = [&](int f) __attribute__((always_inline)) {
+    const int c = f / DB, db = f % DB;
+    const uint32_t ad = vbase[db & 3] + (uint32_t)(16 * c * CPR * 16 + 64 * (db & 4));
+    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)ad);
+    const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(size_t)(ad + 8 * CPR * 16));
+    const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
+    const u32x2 w2 = __builtin_bit_cast(u32x2, t2);
+    return __builtin_bit_cast(V8, u32x4{w1[0], w1[1], w2[0], w2[1]});
+  };
+  constexpr int kNs = 2 * KS;             // S fragments
+  constexpr int kNpv = (kBc / 16) * DB;   // P.V fragments
+
   for (int st = 0; st < nt; ++st) {
     const int kv0 = tile_of(st) * kBc;
     // Wave-uniform classification of this tile for this wave's 32 rows.
@@ -188,17 +242,17 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
     wait_vm_barrier<kLoads>();  // K_j has landed (V_j may still be in flight)
     f32x16 s[2];
     if (active) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const int row = 32 * kb + col;
+      for (int i = 0; i < kPipe; ++i) fr[i] = k_frag(i);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int ch = (2 * ks + hl) ^ swz_k<D>(row);
-          const V8 kf = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(sK + (row * CPR + ch) * 8));
-          s[kb] = E::mfma(kf, qf[ks], s[kb]);
-        }
+      for (int f = 0; f < kNs; ++f) {
+        __builtin_amdgcn_sched_barrier(0);
+        s[f & 1] = E::mfma(fr[f % kPipe], qf[f >> 1], s[f & 1]);
+        if (f + kPipe < kNs) fr[f % kPipe] = k_frag(f + kPipe);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     lds_done_barrier();  // every wave is done with sK
     // The prefetch is issued on every step (the last step re-reads its own
@@ -283,33 +337,21 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
 
     wait_vm_barrier<kKLoads>();  // V_j has landed (K_{j+1} may be in flight)
     if (active) {
-      const int g = lane >> 4;
-      const int L = lane & 15;
 #pragma unroll
-      for (int c = 0; c < kBc / 16; ++c) {
-        const u32x4 bw = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1],
-                          pk[c >> 1][4 * (c & 1) + 2], pk[c >> 1][4 * (c & 1) + 3]};
-        const V8 bop = __builtin_bit_cast(V8, bw);
-        const int kr1 = 16 * c + 4 * (g >> 1) + (L >> 2);
-        const int kr2 = kr1 + 8;
+      for (int i = 0; i < kPipe; ++i) fr[i] = v_frag(i);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int dim = 32 * db + 16 * (g & 1) + 4 * (L & 3);
-          const int ch = dim >> 3;
-          const int hv = (dim >> 2) & 1;
-          const FA2_LDS uint16_t* p1 = sV + (kr1 * CPR + (ch ^ swz_v<D>(kr1))) * 8 + 4 * hv;
-          const FA2_LDS uint16_t* p2 = sV + (kr2 * CPR + (ch ^ swz_v<D>(kr2))) * 8 + 4 * hv;
-          const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)p1);
-          const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)p2);
-          const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
-          const u32x2 w2 = __builtin_bit_cast(u32x2, t2);
-          const u32x4 aw = {w1[0], w1[1], w2[0], w2[1]};
-          o[db] = E::mfma(__builtin_bit_cast(V8, aw), bop, o[db]);
-        }
+      for (int f = 0; f < kNpv; ++f) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int c = f / DB;
+        const u32x4 bw = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1], pk[c >> 1][4 * (c & 1) + 2],
+                          pk[c >> 1][4 * (c & 1) + 3]};
+        o[f % DB] = E::mfma(fr[f % kPipe], __builtin_bit_cast(V8, bw), o[f % DB]);
+        if (f + kPipe < kNpv) fr[f % kPipe] = v_frag(f + kPipe);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     lds_done_barrier();  // every wave is done with sV
-    load_tile<D, true>(vh, sV, kv_next, N, wave, lane);
+    load_v_tile<D>(vh, sV, kv_next, N, wave, lane);
   }
   // No LDS write may still be in flight when the workgroup retires.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

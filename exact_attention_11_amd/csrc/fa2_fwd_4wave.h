@@ -20,7 +20,8 @@
 // plus one v_permlane32_swap); V^T fragments come from the row-major V tile via
 // ds_read_b64_tr_b16; K and V tiles alternate in two single LDS buffers filled
 // by global_load_lds (the next K tile streams under softmax and P.V, the next V
-// tile under the next S); chunks are XOR-swizzled for conflict-free reads.
+// tile under the next S); K is stored in 16-row blocks and V with XOR-swizzled
+// chunks, both for conflict-free reads.
 #pragma once
 
 #include "fa2_common.h"

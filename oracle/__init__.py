@@ -19,6 +19,10 @@ Contents
     The gradients dQ, dK, dV of that definition for a given dO (and the row
     statistic D), by the chain rule in fp64, implemented in
     ``attention_bwd_ref.c``.
+``attention_decode_f64``
+    A few new query rows against a key/value cache with per-batch valid
+    lengths (the last Mq positions of each sequence; causal or not),
+    implemented in ``attention_decode_ref.c``.
 ``tiled``
     A numpy model of the tiled forward recurrence the pages describe (online
     softmax, delayed normalisation, block-level causal skip).  It is used only to
@@ -40,16 +44,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attention_ref.c")
 _BWD_SRC = os.path.join(_HERE, "attention_bwd_ref.c")
 _MASK_SRC = os.path.join(_HERE, "attention_mask_ref.c")
+_DECODE_SRC = os.path.join(_HERE, "attention_decode_ref.c")
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 _lib_cache: dict[str, ctypes.CDLL] = {}
 
 
-def build(src: str = _SRC, out: str = LIB_PATH, bwd_src: str = _BWD_SRC, mask_src: str = _MASK_SRC) -> str:
-    """Compile the C oracle (forward, gradient and general-mask sources) with
-    gcc (no fast-math: IEEE fp64 throughout)."""
+def build(src: str = _SRC, out: str = LIB_PATH, bwd_src: str = _BWD_SRC, mask_src: str = _MASK_SRC,
+          decode_src: str = _DECODE_SRC) -> str:
+    """Compile the C oracle (forward, gradient, general-mask and decode sources)
+    with gcc (no fast-math: IEEE fp64 throughout)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-           "-ffp-contract=off", "-pthread", src, bwd_src, mask_src, "-o", out, "-lm"]
+           "-ffp-contract=off", "-pthread", src, bwd_src, mask_src, decode_src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -79,6 +85,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oracle_attention_masked_f64.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64, i64, ip,
                                                 ctypes.c_double, ctypes.c_int]
     lib.oracle_attention_masked_f64.restype = ctypes.c_int
+    lib.oracle_attention_decode_f64.argtypes = [dp, dp, dp, ip, dp, dp, i64, i64, i64, i64, i64,
+                                                ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.oracle_attention_decode_f64.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
 
@@ -220,4 +229,33 @@ def attention_masked_f64(q, k, v, scale: float, window_left: int = -1, window_ri
                                          _threads(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attention_masked_f64 failed with code {rc}")
+    return o, lse
+
+
+def attention_decode_f64(q, k, v, scale: float, seqlens=None, causal: bool = False,
+                         nthreads: int | None = None, lib_path: str = LIB_PATH):
+    """Exact attention of new query rows q [B, H, Mq, d] against a cache
+    k, v [B, H, Nk, d] whose first ``seqlens[b]`` rows are valid (all Nk when
+    None).  The new rows are the last Mq positions of each sequence: under
+    ``causal`` query i sees keys c <= seqlens[b] - Mq + i.  A query with no
+    visible key gets O = 0 and L = -inf.  Returns ``(o, lse)``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("expected q [B, H, Mq, d] and k, v [B, H, Nk, d]")
+    B, H, Mq, d = q.shape
+    Nk = k.shape[2]
+    len_ptr = None
+    if seqlens is not None:
+        lens = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+        if lens.shape != (B,):
+            raise ValueError("seqlens must be [B]")
+        len_ptr = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    o = np.empty_like(q)
+    lse = np.empty((B, H, Mq), dtype=np.float64)
+    lib = load(lib_path)
+    rc = lib.oracle_attention_decode_f64(_ptr(q), _ptr(k), _ptr(v), len_ptr, _ptr(o), _ptr(lse), B, H, Mq, Nk, d,
+                                         int(bool(causal)), float(scale), _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_decode_f64 failed with code {rc}")
     return o, lse

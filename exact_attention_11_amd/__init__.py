@@ -1,5 +1,5 @@
-"""Fused exact attention for AMD Instinct MI355X (gfx950): forward pass and
-gradients.
+"""Fused exact attention for AMD Instinct MI355X (gfx950): forward pass,
+gradients, and decode against a key/value cache.
 
 Thin Python binding of the C ABI declared in ``include/fa2.h``; every step of
 the computation runs in the HIP kernels of ``libfa2.so``.  torch supplies device
@@ -7,6 +7,7 @@ memory and streams only.
 
     o, lse = exact_attention_11_amd.forward(q, k, v, causal=True)
     dq, dk, dv = exact_attention_11_amd.backward(q, k, v, o, do, lse, causal=True)
+    o1, lse1 = exact_attention_11_amd.decode(q1, k_cache, v_cache, seqlens=lens)
 
 ``q, k, v``: [B, H, N, d] fp16 or bf16 CUDA (HIP) tensors, contiguous.
 ``forward`` returns ``o`` (same shape and dtype) and ``lse`` ([B, H, N] float32,
@@ -36,9 +37,12 @@ FA2_ERR_ALIAS = 7
 FA2_ERR_DEVICE = 8
 FA2_ERR_LAUNCH = 9
 FA2_ERR_MASK = 10
+FA2_ERR_WORKSPACE = 11
 
 # Every symbol include/fa2.h declares.
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_bwd", "fa2_status_str", "fa2_last_hip_error")
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_bwd", "fa2_decode", "fa2_decode_workspace_bytes",
+                    "fa2_status_str", "fa2_last_hip_error")
+DECODE_MAX_QUERIES = 8
 
 
 class Fa2Mask(ctypes.Structure):
@@ -82,6 +86,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                             ctypes.c_float, ctypes.c_int, vp]
     lib.fa2_bwd.restype = ctypes.c_int
+    lib.fa2_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                               ctypes.c_int, vp, i64, vp]
+    lib.fa2_decode.restype = ctypes.c_int
+    lib.fa2_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.fa2_decode_workspace_bytes.restype = i64
     lib.fa2_status_str.argtypes = [ctypes.c_int]
     lib.fa2_status_str.restype = ctypes.c_char_p
     lib.fa2_last_hip_error.argtypes = []
@@ -110,6 +119,19 @@ def fa2_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, delta: int, dq:
     """Direct call of the gradient entry point with raw device addresses; returns the status."""
     return load_library().fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, int(causal),
                                   float(scale), int(dtype), stream)
+
+
+def fa2_decode(q: int, k: int, v: int, seqlens: int | None, o: int, lse: int, B: int, H: int, Mq: int, Nk: int,
+               d: int, causal: int, scale: float, dtype: int, workspace: int | None, workspace_bytes: int,
+               stream: int) -> int:
+    """Direct call of the decode entry point with raw device addresses; returns the status."""
+    return load_library().fa2_decode(q, k, v, seqlens, o, lse, B, H, Mq, Nk, d, int(causal), float(scale),
+                                     int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def fa2_decode_workspace_bytes(B: int, H: int, Mq: int, Nk: int, d: int) -> int:
+    """Workspace bytes fa2_decode needs (0: none), or minus a status code."""
+    return load_library().fa2_decode_workspace_bytes(B, H, Mq, Nk, d)
 
 
 def fa2_status_str(status: int) -> str:
@@ -229,3 +251,60 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
     if rc != FA2_OK:
         raise Fa2Error(rc, fa2_status_str(rc), "fa2_bwd")
     return dq, dk, dv
+
+
+def decode(q, k, v, seqlens=None, causal: bool = False, scale: float | None = None, out=None, lse=None,
+           stream=None, workspace=None):
+    """Decode on the GPU: ``q`` [B, H, Mq, d] (1 <= Mq <= 8 new rows) against the
+    cache ``k, v`` [B, H, Nk, d], of which the first ``seqlens[b]`` rows are
+    valid (``seqlens``: int32 [B] on the device, or None for all Nk).  The new
+    rows are the last Mq positions of each sequence; under ``causal`` query i
+    sees keys c <= seqlens[b] - Mq + i.  Returns ``(o, lse)``; a query with no
+    visible key gets o = 0 and lse = -inf.  ``workspace`` (a uint8 device
+    tensor of at least ``fa2_decode_workspace_bytes`` bytes) is allocated here
+    when needed and not given.
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"expected q [B, H, Mq, d] and k, v [B, H, Nk, d], got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    code = _dtype_code(q)
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, Mq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    len_ptr = None
+    if seqlens is not None:
+        if (seqlens.shape != (B,) or seqlens.dtype != torch.int32 or not seqlens.is_contiguous()
+                or seqlens.device != q.device):
+            raise ValueError("seqlens must be a contiguous int32 [B] tensor on q's device")
+        len_ptr = seqlens.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Mq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, Mq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, Mq] tensor on q's device")
+    need = fa2_decode_workspace_bytes(B, H, Mq, Nk, d)
+    if need < 0:
+        raise Fa2Error(-need, fa2_status_str(-need), "fa2_decode")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = fa2_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), len_ptr, out.data_ptr(), lse.data_ptr(),
+                        B, H, Mq, Nk, d, int(bool(causal)), float(scale), code, ws_ptr, ws_bytes, s.cuda_stream)
+    if rc != FA2_OK:
+        raise Fa2Error(rc, fa2_status_str(rc), "fa2_decode")
+    return out, lse

@@ -1,9 +1,9 @@
-// fa2_api.hip -- C ABI of the fused attention forward pass and of its
-// gradients (declared in include/fa2.h): argument checks, device check,
-// instance dispatch and launch.
+// fa2_api.hip -- C ABI of the fused attention forward pass, of its gradients
+// and of decode against a key/value cache (declared in include/fa2.h): argument
+// checks, device check, instance dispatch and launch.
 //
-// Instances: element type {fp16, bf16} x head dim {64, 128, 256} x {no mask,
-// causal}.  The head-dim limit of 256 follows "FlashAttention-2: Where the Second
+// Forward instances: element type {fp16, bf16} x head dim {64, 128, 256} x mask
+// {none, causal, window/prefix, window/prefix/segment ids}.  The head-dim limit of 256 follows "FlashAttention-2: Where the Second
 // 2x Actually Comes From" (section "Limitations & open questions").
 #include <hip/hip_runtime.h>
 
@@ -13,6 +13,7 @@
 
 #include "fa2.h"
 #include "fa2_bwd.h"
+#include "fa2_decode.h"
 #include "fa2_fwd_4wave.h"
 #include "fa2_fwd_8wave.h"
 
@@ -113,6 +114,80 @@ hipError_t launch_bwd_d(const fa2::bwd::BwdArgs& args, int64_t d, bool causal, h
   }
 }
 
+// Decode plan: chunks per (batch, head) so that about kDecodeWgTarget
+// workgroups stream the cache (4 per CU), chunks of at least kDecodeMinChunk
+// keys, a multiple of 64.
+constexpr int64_t kDecodeWgTarget = 1024;
+constexpr int64_t kDecodeMinChunk = 256;
+struct DecodePlan {
+  int64_t n_split, chunk;
+};
+DecodePlan decode_plan(int64_t bh, int64_t Nk) {
+  int64_t n = (kDecodeWgTarget + bh - 1) / bh;
+  const int64_t most = (Nk + kDecodeMinChunk - 1) / kDecodeMinChunk;
+  if (n > most) n = most;
+  if (n < 1) n = 1;
+  int64_t chunk = (Nk + n - 1) / n;
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk < 64) chunk = 64;
+  n = (Nk + chunk - 1) / chunk;
+  if (n < 1) n = 1;
+  return {n, chunk};
+}
+
+// Shape checks shared by fa2_decode and fa2_decode_workspace_bytes; FA2_OK or
+// an error status.
+int decode_shape_status(int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d) {
+  if (B < 0 || H < 0 || Mq < 0 || Nk < 0) return FA2_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA2_ERR_HEADDIM;
+  if (Mq > fa2::dec::kMaxQ) return FA2_ERR_SHAPE;
+  if (B > INT32_MAX || H > INT32_MAX || Nk > (int64_t)INT32_MAX - 65536) return FA2_ERR_SHAPE;
+  const int64_t bh = B * H;
+  if (bh == 0 || Mq == 0) return FA2_OK;
+  if (bh > (int64_t)INT32_MAX / 64) return FA2_ERR_SHAPE;
+  const DecodePlan p = decode_plan(bh, Nk);
+  if (p.n_split * bh > (int64_t)INT32_MAX || bh * Mq > (int64_t)INT32_MAX) return FA2_ERR_SHAPE;
+  if (Nk > 0 && bh > (INT64_MAX / 4) / (Nk * d)) return FA2_ERR_SHAPE;
+  return FA2_OK;
+}
+
+int64_t decode_workspace(int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d) {
+  const int64_t bh = B * H;
+  if (bh == 0 || Mq == 0) return 0;
+  const DecodePlan p = decode_plan(bh, Nk);
+  if (p.n_split == 1) return 0;
+  return p.n_split * bh * Mq * (d + 1) * 4;  // partial outputs, then partial logsumexp
+}
+
+template <int kDType, int D, int MQ>
+hipError_t launch_decode(const fa2::dec::DecArgs& args, hipStream_t stream) {
+  using namespace fa2::dec;
+  hipLaunchKernelGGL((fa2_decode_split<kDType, D, MQ>), dim3((unsigned)(args.n_split * args.n_bh)), dim3(kThreads),
+                     0, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || args.n_split == 1) return e;
+  hipLaunchKernelGGL((fa2_decode_combine<kDType, D>), dim3((unsigned)(args.n_bh * args.Mq)), dim3(D), 0, stream,
+                     args);
+  return hipGetLastError();
+}
+
+template <int kDType, int D>
+hipError_t launch_decode_q(const fa2::dec::DecArgs& args, hipStream_t stream) {
+  if (args.Mq <= 1) return launch_decode<kDType, D, 1>(args, stream);
+  if (args.Mq <= 2) return launch_decode<kDType, D, 2>(args, stream);
+  if (args.Mq <= 4) return launch_decode<kDType, D, 4>(args, stream);
+  return launch_decode<kDType, D, 8>(args, stream);
+}
+
+template <int kDType>
+hipError_t launch_decode_d(const fa2::dec::DecArgs& args, int64_t d, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_decode_q<kDType, 64>(args, stream);
+    case 128: return launch_decode_q<kDType, 128>(args, stream);
+    default: return launch_decode_q<kDType, 256>(args, stream);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,6 +205,7 @@ const char* fa2_status_str(int status) {
     case FA2_ERR_DEVICE: return "no usable gfx950 device";
     case FA2_ERR_LAUNCH: return "kernel launch failed";
     case FA2_ERR_MASK: return "mask: window bound below -1, negative prefix or misaligned segment ids";
+    case FA2_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
     default: return "unknown status";
   }
 }
@@ -290,6 +366,75 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_bwd_d<0>(args, d, causal != 0, s)
                                          : launch_bwd_d<1>(args, d, causal != 0, s);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA2_ERR_LAUNCH;
+  }
+  return FA2_OK;
+}
+
+int64_t fa2_decode_workspace_bytes(int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d) {
+  const int st = decode_shape_status(B, H, Mq, Nk, d);
+  if (st != FA2_OK) return -(int64_t)st;
+  return decode_workspace(B, H, Mq, Nk, d);
+}
+
+int fa2_decode(const void* q, const void* k, const void* v, const int32_t* seqlens, void* o, float* lse, int64_t B,
+               int64_t H, int64_t Mq, int64_t Nk, int64_t d, int causal, float scale, int dtype, void* workspace,
+               int64_t workspace_bytes, void* stream) {
+  g_last_hip_error = 0;
+  // ---- argument checks: no HIP call before they all pass -------------------
+  const int st = decode_shape_status(B, H, Mq, Nk, d);
+  if (st != FA2_OK) return st;
+  if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
+  const float c2 = (float)((double)scale * 1.4426950408889634074);
+  if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
+  const int64_t bh = B * H;
+  if (bh == 0 || Mq == 0) return FA2_OK;
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA2_ERR_NULLPTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA2_ERR_ALIGN;
+  if (((uintptr_t)seqlens) & 3) return FA2_ERR_ALIGN;
+  const int64_t need = decode_workspace(B, H, Mq, Nk, d);
+  if (need > 0 && (!workspace || workspace_bytes < need || (((uintptr_t)workspace) & 15))) return FA2_ERR_WORKSPACE;
+  const uint64_t qb = (uint64_t)(bh * Mq * d) * 2, kb = (uint64_t)(bh * Nk * d) * 2;
+  const uint64_t lb = (uint64_t)(bh * Mq) * 4, sb = seqlens ? (uint64_t)B * 4 : 0, wb = (uint64_t)need;
+  const void* in[4] = {q, k, v, seqlens};
+  const uint64_t in_n[4] = {qb, kb, kb, sb};
+  const void* out[3] = {o, lse, workspace};
+  const uint64_t out_n[3] = {qb, lb, wb};
+  for (int i = 0; i < 3; ++i) {
+    if (out_n[i] == 0) continue;
+    for (int j = 0; j < 4; ++j)
+      if (in_n[j] > 0 && overlaps(out[i], out_n[i], in[j], in_n[j])) return FA2_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (out_n[j] > 0 && overlaps(out[i], out_n[i], out[j], out_n[j])) return FA2_ERR_ALIAS;
+  }
+
+  // ---- device ---------------------------------------------------------------
+  const int dev_status = check_device();
+  if (dev_status != FA2_OK) return dev_status;
+
+  const DecodePlan plan = decode_plan(bh, Nk);
+  fa2::dec::DecArgs args;
+  args.q = (const uint16_t*)q;
+  args.k = (const uint16_t*)k;
+  args.v = (const uint16_t*)v;
+  args.o = (uint16_t*)o;
+  args.lse = lse;
+  args.seqlens = seqlens;
+  args.part_o = need > 0 ? (float*)workspace : nullptr;
+  args.part_lse = need > 0 ? (float*)workspace + plan.n_split * bh * Mq * d : nullptr;
+  args.H = (int)H;
+  args.Mq = (int)Mq;
+  args.Nk = (int)Nk;
+  args.n_split = (int)plan.n_split;
+  args.chunk = (int)plan.chunk;
+  args.causal = causal != 0;
+  args.n_bh = (int)bh;
+  args.c2 = c2;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_decode_d<0>(args, d, s) : launch_decode_d<1>(args, d, s);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FA2_ERR_LAUNCH;

@@ -80,3 +80,69 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype, dist: str = "normal", seed: 
 
 def workload_inputs(w: Workload, seed: int = 0):
     return make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, w.dist, seed)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H: int
+    Mq: int        # new query rows per (batch, head)
+    Nk: int        # cache capacity
+    d: int
+    dtype: str     # "fp16" or "bf16"
+    causal: bool
+    lengths: str   # "full": every cache row valid; "ragged": lengths drawn uniformly from [1, Nk]
+    what: str
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "fp16" else torch.bfloat16
+
+
+# Decode against a cache as long as the longest forward workload (16384 tokens,
+# head dim 128): a batch of 8 sequences x 32 heads, one new token each.
+DECODE_WORKLOADS = {
+    w.name: w for w in [
+        DecodeWorkload("decode_b8h32_m1_n16384_d128", 8, 32, 1, 16384, 128, "fp16", True, "full",
+                       "batch 8 x 32 heads, 1 new token against a 16384-token cache, head dim 128"),
+        DecodeWorkload("decode_b8h32_m1_n16384_d128_ragged", 8, 32, 1, 16384, 128, "fp16", True, "ragged",
+                       "batch 8 x 32 heads, 1 new token against caches of 1-16384 valid tokens, head dim 128"),
+        DecodeWorkload("decode_b1h32_m4_n16384_d128", 1, 32, 4, 16384, 128, "bf16", True, "full",
+                       "batch 1 x 32 heads, 4 new tokens (causal) against a 16384-token cache, head dim 128"),
+    ]
+}
+
+
+def make_decode_inputs(B: int, H: int, Mq: int, Nk: int, d: int, dtype, seed: int = 0):
+    """Host tensors q [B, H, Mq, d] and k, v [B, H, Nk, d] in ``dtype``: i.i.d.
+    N(0, 1) drawn in fp32 from ``torch.Generator('cpu').manual_seed(seed)`` in
+    the order Q, K, V, rounded once to ``dtype``."""
+    if isinstance(dtype, str):
+        dtype = torch.float16 if dtype == "fp16" else torch.bfloat16
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((B, H, Mq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32)
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+def decode_lengths(B: int, Nk: int, kind: str, seed: int = 0):
+    """int32 host tensor [B] of valid cache lengths: "full" (all Nk) or
+    "ragged" (uniform on [1, Nk], seeded)."""
+    if kind == "full":
+        return torch.full((B,), Nk, dtype=torch.int32)
+    if kind == "ragged":
+        g = torch.Generator("cpu").manual_seed(10_000 + seed)
+        return torch.randint(1, max(Nk, 1) + 1, (B,), generator=g, dtype=torch.int32)
+    raise ValueError(kind)
+
+
+def decode_workload_inputs(w: DecodeWorkload, seed: int = 0):
+    q, k, v = make_decode_inputs(w.B, w.H, w.Mq, w.Nk, w.d, w.torch_dtype, seed)
+    return q, k, v, decode_lengths(w.B, w.Nk, w.lengths, seed)
+

@@ -51,8 +51,10 @@ typedef enum {
   FA2_ERR_ALIAS = 7,   /* an output overlaps an input or another output */
   FA2_ERR_DEVICE = 8,  /* no current HIP device, or it is not a gfx950 */
   FA2_ERR_LAUNCH = 9,  /* the HIP launch itself reported an error */
-  FA2_ERR_MASK = 10    /* fa2_fwd_masked: a window bound below -1, a negative
+  FA2_ERR_MASK = 10,   /* fa2_fwd_masked: a window bound below -1, a negative
                           prefix, or segment ids not 4-byte aligned */
+  FA2_ERR_WORKSPACE = 11 /* fa2_decode: the workspace it needs is missing, smaller
+                            than fa2_decode_workspace_bytes, or not 16-byte aligned */
 } fa2_status;
 
 /*
@@ -159,11 +161,60 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const vo
             int64_t B, int64_t H, int64_t N, int64_t d,
             int causal, float scale, int dtype, void* stream);
 
+/*
+ * fa2_decode -- enqueue decode against a key/value cache on `stream` and return
+ * without waiting: Mq new query rows per (batch, head) attend to the first
+ * len_b rows of the cache of their (batch, head), len_b = seqlens[b] (clamped
+ * to [0, Nk]) or Nk when seqlens is NULL.  The new rows are the last Mq
+ * positions of a sequence of len_b tokens; with causal != 0 query i (0-based)
+ * sees keys c <= len_b - Mq + i, otherwise every key c < len_b:
+ *
+ *   O[b,h,i,:] = sum_c softmax_c(scale * q_i . k_c) v_c,   L[b,h,i] = log sum_c exp(scale * q_i . k_c)
+ *
+ * over the visible keys (natural log; a query with no visible key gets O = 0
+ * and L = -inf).
+ *  - One query row against the cached keys and values is the single-token
+ *    decoding regime that "Flash Attention: Memory-Efficient Attention at
+ *    Scale", section "Common misconceptions", sets apart (Flash-Decoding).
+ *  - The cache is split into chunks processed in parallel; each chunk's
+ *    normalised output and logsumexp merge exactly through the row max and sum,
+ *    the online-softmax rule of "6.2 FlashAttention V2 in depth", sections 3.2
+ *    and 6.1.
+ *
+ * q         : [B, H, Mq, d] `dtype`, device, read only; 1 <= Mq <= 8.
+ * k, v      : [B, H, Nk, d] `dtype`, device, read only (the cache; rows past a
+ *             batch's length are never used).
+ * seqlens   : [B] int32, device, read only, 4-byte aligned; or NULL.
+ * o, lse    : [B, H, Mq, d] `dtype` and [B, H, Mq] float32, device, written.
+ * workspace : device memory of at least fa2_decode_workspace_bytes(B, H, Mq,
+ *             Nk, d) bytes, 16-byte aligned, owned by the caller, overwritten;
+ *             NULL is allowed when that size is 0.  Its contents between
+ *             calls do not matter.
+ * B, H, Nk, d, causal, scale, dtype, stream: as for fa2_fwd (d in {64, 128,
+ *             256}); Nk = 0 is allowed (every row then has no visible key).
+ *
+ * Returns FA2_OK, or FA2_ERR_SHAPE (Mq outside [0, 8], negative or too large
+ * sizes), FA2_ERR_HEADDIM, FA2_ERR_DTYPE, FA2_ERR_SCALE, FA2_ERR_NULLPTR,
+ * FA2_ERR_ALIGN (q, k, v, o, lse not 16-byte aligned; seqlens not 4-byte
+ * aligned), FA2_ERR_WORKSPACE, FA2_ERR_ALIAS (o, lse or the workspace overlap
+ * an input or each other), FA2_ERR_DEVICE, FA2_ERR_LAUNCH.  B*H*Mq = 0 is a
+ * no-op.  One or two kernels run in order on `stream`; results are bitwise
+ * reproducible.
+ */
+int fa2_decode(const void* q, const void* k, const void* v, const int32_t* seqlens,
+               void* o, float* lse, int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d,
+               int causal, float scale, int dtype, void* workspace, int64_t workspace_bytes,
+               void* stream);
+
+/* Bytes of workspace fa2_decode needs for these sizes (0: none), or minus a
+ * fa2_status code for sizes fa2_decode would reject.  Host only; no HIP call. */
+int64_t fa2_decode_workspace_bytes(int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d);
+
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char* fa2_status_str(int status);
 
-/* Last HIP error code seen by a failing fa2_fwd, fa2_fwd_masked or fa2_bwd call
- * on this thread (0 if none); useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
+/* Last HIP error code seen by a failing fa2_fwd, fa2_fwd_masked, fa2_bwd or
+ * fa2_decode call on this thread (0 if none); useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
 int fa2_last_hip_error(void);
 
 #ifdef __cplusplus

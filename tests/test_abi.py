@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = fa.fa2_status_str(code)
         assert s and s != "unknown status"
     assert fa.fa2_status_str(123) == "unknown status"
@@ -198,3 +198,75 @@ def test_masked_valid_call_without_device_reports_device_error(lib):
     for mask in (None, fa.Fa2Mask(1, 5, 0, 3, 0x60000000), fa.Fa2Mask(0, -1, -1, 0, None)):
         for d in (64, 128, 256):
             assert _masked(mask, d=d, N=333) == fa.FA2_ERR_DEVICE
+
+
+# --- fa2_decode --------------------------------------------------------------------
+
+SL, WS = 0xB0000000, 0xC0000000
+
+
+def _dec(B=1, H=1, Mq=1, Nk=16, d=64, causal=0, scale=0.125, dtype=0, q=Q, k=K, v=V, seqlens=SL, o=O, lse=L,
+         ws=WS, ws_bytes=1 << 20):
+    return fa.fa2_decode(q, k, v, seqlens, o, lse, B, H, Mq, Nk, d, causal, scale, dtype, ws, ws_bytes, None)
+
+
+def test_decode_workspace_sizes(lib):
+    # small caches need no split; a long cache of one head splits into chunks
+    # of at least 256 keys, each with d + 1 floats per query row
+    assert fa.fa2_decode_workspace_bytes(1, 1, 1, 16, 64) == 0
+    assert fa.fa2_decode_workspace_bytes(1, 1, 1, 4096, 64) == 16 * 1 * 1 * 65 * 4
+    assert fa.fa2_decode_workspace_bytes(2, 4, 3, 4096, 128) == 16 * 8 * 3 * 129 * 4
+    assert fa.fa2_decode_workspace_bytes(8, 32, 1, 16384, 128) == 4 * 256 * 129 * 4
+    assert fa.fa2_decode_workspace_bytes(64, 64, 1, 16384, 128) == 0  # 4096 heads fill the chip alone
+    assert fa.fa2_decode_workspace_bytes(0, 4, 1, 4096, 128) == 0
+    assert fa.fa2_decode_workspace_bytes(1, 1, 9, 16, 64) == -fa.FA2_ERR_SHAPE
+    assert fa.fa2_decode_workspace_bytes(1, 1, 1, 16, 96) == -fa.FA2_ERR_HEADDIM
+    assert fa.fa2_decode_workspace_bytes(-1, 1, 1, 16, 64) == -fa.FA2_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(B=-1), fa.FA2_ERR_SHAPE), (dict(Mq=-1), fa.FA2_ERR_SHAPE), (dict(Mq=9), fa.FA2_ERR_SHAPE),
+    (dict(Nk=-1), fa.FA2_ERR_SHAPE), (dict(Nk=2 ** 31), fa.FA2_ERR_SHAPE),
+    (dict(d=32), fa.FA2_ERR_HEADDIM), (dict(dtype=2), fa.FA2_ERR_DTYPE), (dict(scale=math.nan), fa.FA2_ERR_SCALE),
+    (dict(q=0), fa.FA2_ERR_NULLPTR), (dict(k=0), fa.FA2_ERR_NULLPTR), (dict(o=0), fa.FA2_ERR_NULLPTR),
+    (dict(lse=0), fa.FA2_ERR_NULLPTR),
+    (dict(q=Q + 8), fa.FA2_ERR_ALIGN), (dict(lse=L + 4), fa.FA2_ERR_ALIGN), (dict(seqlens=SL + 2), fa.FA2_ERR_ALIGN),
+    (dict(Nk=4096, ws=0), fa.FA2_ERR_WORKSPACE), (dict(Nk=4096, ws_bytes=4159), fa.FA2_ERR_WORKSPACE),
+    (dict(Nk=4096, ws=WS + 8), fa.FA2_ERR_WORKSPACE),
+    (dict(o=Q), fa.FA2_ERR_ALIAS), (dict(o=K + 64), fa.FA2_ERR_ALIAS), (dict(lse=SL), fa.FA2_ERR_ALIAS),
+    (dict(lse=O + 64), fa.FA2_ERR_ALIAS), (dict(Nk=4096, ws=V + 1024), fa.FA2_ERR_ALIAS),
+    (dict(Nk=4096, ws=O), fa.FA2_ERR_ALIAS),
+])
+def test_decode_argument_checks(lib, kwargs, code):
+    assert _dec(**kwargs) == code
+
+
+@pytest.mark.parametrize("kwargs", [dict(B=0), dict(H=0), dict(Mq=0), dict(Mq=0, q=0, k=0, o=0, lse=0)])
+def test_decode_empty_problem_is_a_no_op(lib, kwargs):
+    assert _dec(**kwargs) == fa.FA2_OK
+
+
+def test_decode_valid_call_without_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    for d in (64, 128, 256):
+        for Mq in (1, 3, 8):
+            assert _dec(d=d, Mq=Mq, Nk=5000, causal=1, dtype=1) == fa.FA2_ERR_DEVICE
+    # no workspace is needed without a split, and none without a cache
+    assert _dec(ws=0, ws_bytes=0) == fa.FA2_ERR_DEVICE
+    assert _dec(Nk=0, k=0, v=0, ws=0, ws_bytes=0) == fa.FA2_ERR_DEVICE
+    assert _dec(seqlens=0) == fa.FA2_ERR_DEVICE
+
+
+def test_python_decode_rejects_bad_tensors(lib):
+    import torch
+    q = torch.zeros(1, 2, 1, 64, dtype=torch.float16)
+    kv = torch.zeros(1, 2, 16, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.decode(q, kv, kv)  # host tensors
+    with pytest.raises(ValueError):
+        fa.decode(q, kv[:, :1], kv)
+    with pytest.raises(TypeError):
+        fa.decode(q.float(), kv.float(), kv.float())
+

@@ -28,6 +28,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth, published
+DEFAULT_DECODE_WORKLOAD = "decode_b8h32_m1_n16384_d128"
 DEFAULT_WORKLOAD = "b1h32_n16384_d128_causal"
 PROFILES = os.path.join(ROOT, "profiles")
 # The sources that define the kernels of each pass (a recorded profile applies
@@ -36,6 +38,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
                   for f in ("fa2_common.h", "fa2_fwd_4wave.h", "fa2_fwd_8wave.h")]
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
                       for f in ("fa2_common.h", "fa2_bwd.h")]
+DECODE_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
+                         for f in ("fa2_common.h", "fa2_decode.h")]
 
 
 def log(msg: str) -> None:
@@ -186,6 +190,137 @@ def cpu_baseline_bwd(w, q, k, v, dout, target_s: float = 12.0):
     }
 
 
+def decode_bytes(w, lens) -> float:
+    """Compulsory HBM bytes of one decode call: every visible cache row of K and
+    V read once (the last new row of a sequence sees all of its len_b rows), Q
+    read once, O and L written once."""
+    rows = float(sum(int(x) for x in lens))
+    kv = 2.0 * rows * w.H * w.d * 2
+    qo = 2.0 * w.B * w.H * w.Mq * w.d * 2
+    return kv + qo + w.B * w.H * w.Mq * 4
+
+
+def cpu_baseline_decode(w, q, k, v, lens, target_s: float = 12.0):
+    """Time the fp64 decode oracle on whole (batch, head) pairs, one pair per host
+    thread per call (the oracle works a (batch, head) pair per thread), until
+    about ``target_s`` seconds have passed."""
+    import numpy as np
+
+    import oracle
+
+    threads = host_threads()
+    scale = float(np.float32(w.scale))
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, nbytes, secs = 0, 0.0, 0.0
+    while done < len(pairs) and secs < target_s:
+        batch = pairs[done:done + threads]
+        # the pairs as a batch of single-head sequences with their own lengths
+        qs = np.stack([q[b, h].double().numpy() for b, h in batch])[:, None]
+        ks = np.stack([k[b, h].double().numpy() for b, h in batch])[:, None]
+        vs = np.stack([v[b, h].double().numpy() for b, h in batch])[:, None]
+        lens_b = [int(lens[b]) for b, _ in batch]
+        t0 = time.perf_counter()
+        oracle.attention_decode_f64(qs, ks, vs, scale, seqlens=lens_b, causal=w.causal, nthreads=threads)
+        secs += time.perf_counter() - t0
+        nbytes += 2.0 * sum(lens_b) * w.d * 2
+        done += len(batch)
+    return {
+        "value": nbytes / secs / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} (batch, head) pair(s) of {w.name}: {nbytes / 1e9:.2f} GB of fp16/bf16 cache rows in "
+                  f"{secs:.1f} s (fp64 decode oracle)",
+    }
+
+
+def time_steps(step, stream, args):
+    """Warm up (fixed count, then until min_warmup_ms has passed), then time
+    args.steps calls with HIP events on ``stream``.  Returns (ms_per_step,
+    avg_launch_ms, min_launch_ms, wall_ms_per_step, extra_warmup_steps)."""
+    import torch
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    extra = 0
+    t_w0 = time.perf_counter()
+    while (time.perf_counter() - t_w0) * 1e3 < args.min_warmup_ms:
+        for _ in range(5):
+            step()
+        extra += 5
+        torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall0
+    launch_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    total_ms = starts[0].elapsed_time(ends[-1])
+    return total_ms / args.steps, sum(launch_ms) / len(launch_ms), min(launch_ms), wall_s * 1e3 / args.steps, extra
+
+
+def run_decode(args) -> int:
+    import torch
+
+    import exact_attention_11_amd as fa
+    from exact_attention_11_amd.inputs import DECODE_WORKLOADS, decode_workload_inputs
+
+    name = args.workload if args.workload in DECODE_WORKLOADS else DEFAULT_DECODE_WORKLOAD
+    w = DECODE_WORKLOADS[name]
+    log(f"workload {w.name}: {w.what} (decode)")
+    q, k, v, lens = decode_workload_inputs(w, seed=0)
+    dq, dk, dv, dl = q.cuda(), k.cuda(), v.cuda(), lens.cuda()
+    o = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.H, w.Mq), dtype=torch.float32, device="cuda")
+    need = fa.fa2_decode_workspace_bytes(w.B, w.H, w.Mq, w.Nk, w.d)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.decode(dq, dk, dv, seqlens=dl, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream,
+                  workspace=ws)
+
+    nbytes = decode_bytes(w, lens.tolist())
+    ms_per_step, avg_ms, min_ms, wall_ms, extra = time_steps(step, stream, args)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    log(f"{args.steps} steps: {ms_per_step:.4f} ms/step (events), launch avg {avg_ms:.4f} ms, min {min_ms:.4f} ms, "
+        f"wall {wall_ms:.4f} ms/step -> {value:.1f} GB/s")
+    result = {
+        "metric": "decode GB/s of compulsory HBM traffic (cache rows, Q, O, L), % of MI355X 8 TB/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "clock_warmup_steps": extra,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "decode", "B": w.B, "H": w.H, "Mq": w.Mq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "lengths": w.lengths, "bytes_per_step": nbytes, "workspace_bytes": need,
+                   "kernel_source_digest": kernel_source_digest(DECODE_KERNEL_SOURCES)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of the workload ...")
+        result["cpu_baseline"] = cpu_baseline_decode(w, q, k, v, lens.tolist(), args.cpu_seconds)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,8 +334,9 @@ def main() -> int:
     ap.add_argument("--prefix", type=int, default=0, help="forward pass: keys below this are visible to every query")
     ap.add_argument("--documents", type=int, default=0,
                     help="forward pass: split each sequence into this many equal contiguous documents")
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
-                    help="time the forward pass (the headline) or the gradient pass of the workload")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "decode"), default="fwd",
+                    help="time the forward pass (the headline), the gradient pass of the workload, or decode "
+                         "against a key/value cache (a decode workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -228,9 +364,11 @@ def main() -> int:
         log(f"copied {n} bytes 5 times")
         return 0
 
-    if args.pass_ == "bwd" and (args.window is not None or args.prefix > 0 or args.documents > 0):
-        log("the gradient pass supports the causal mask and no mask only")
+    if args.pass_ != "fwd" and (args.window is not None or args.prefix > 0 or args.documents > 0):
+        log("masks other than causal apply to the forward pass only")
         return 2
+    if args.pass_ == "decode":
+        return run_decode(args)
 
     import exact_attention_11_amd as fa
     from exact_attention_11_amd.inputs import WORKLOADS, workload_inputs
@@ -283,38 +421,15 @@ def main() -> int:
         flop = 2.5 * flop_count(w.B, w.H, w.N, w.d, w.causal)
         metric = "attention bwd TFLOP/s (5 products per pair) and % of MI355X FP16/BF16 MFMA peak"
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     # The engine clock ramps up over the first tens of milliseconds of MFMA load;
-    # keep running untimed steps until the warm-up has lasted min_warmup_ms so the
-    # timed steps see the steady clock (the count is reported in the JSON line).
-    extra = 0
-    t_w0 = time.perf_counter()
-    while (time.perf_counter() - t_w0) * 1e3 < args.min_warmup_ms:
-        for _ in range(5):
-            step()
-        extra += 5
-        torch.cuda.synchronize()
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t_wall0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    total_ms = starts[0].elapsed_time(ends[-1])
-    ms_per_step = total_ms / args.steps
-    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    # time_steps keeps running untimed steps until the warm-up has lasted
+    # min_warmup_ms so the timed steps see the steady clock (the count is
+    # reported in the JSON line).
+    ms_per_step, avg_launch_ms, min_ms, wall_ms, extra = time_steps(step, stream, args)
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
     log(f"{args.steps} steps: {ms_per_step:.4f} ms/step (events), launch avg {avg_launch_ms:.4f} ms, "
-        f"min {min(launch_ms):.4f} ms, wall {wall_s * 1e3 / args.steps:.4f} ms/step -> {value:.1f} TFLOP/s")
+        f"min {min_ms:.4f} ms, wall {wall_ms:.4f} ms/step -> {value:.1f} TFLOP/s")
 
     traffic = recorded_traffic(w.name) if args.pass_ == "fwd" and not masked else None
     result = {

@@ -82,16 +82,16 @@ def kernel_source_digest(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, summary: str | None = None, sources=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(PROFILES, f"fa2_fwd_{workload}_hbm_traffic.md")
+    path = os.path.join(PROFILES, summary or f"fa2_fwd_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_src = re.search(r"kernel_source_digest:\s*(\w+)", text)
     m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_src or not m_val or m_src.group(1) != kernel_source_digest():
+    if not m_src or not m_val or m_src.group(1) != kernel_source_digest(sources):
         return None
     return float(m_val.group(1))
 
@@ -310,7 +310,9 @@ def run_decode(args) -> int:
                    "causal": w.causal, "lengths": w.lengths, "bytes_per_step": nbytes, "workspace_bytes": need,
                    "kernel_source_digest": kernel_source_digest(DECODE_KERNEL_SOURCES)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": recorded_traffic(w.name, f"fa2_decode_{w.name[len('decode_'):]}_kernel_stats.md",
+                                                 DECODE_KERNEL_SOURCES)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

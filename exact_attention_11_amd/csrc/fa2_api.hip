@@ -115,9 +115,10 @@ hipError_t launch_bwd_d(const fa2::bwd::BwdArgs& args, int64_t d, bool causal, h
 }
 
 // Decode plan: chunks per (batch, head) so that about kDecodeWgTarget
-// workgroups stream the cache (4 per CU), chunks of at least kDecodeMinChunk
-// keys, a multiple of 64.
-constexpr int64_t kDecodeWgTarget = 1024;
+// workgroups stream the cache (2 per CU, each wave with 2 x 16 row loads in
+// flight; 1024 or 2048 workgroups measured slower on short and ragged caches),
+// chunks of at least kDecodeMinChunk keys, a multiple of 64.
+constexpr int64_t kDecodeWgTarget = 512;
 constexpr int64_t kDecodeMinChunk = 256;
 struct DecodePlan {
   int64_t n_split, chunk;

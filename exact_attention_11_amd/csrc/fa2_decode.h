@@ -79,7 +79,7 @@ template <int kDType, int D, int MQ>
 __global__ __launch_bounds__(kThreads) void fa2_decode_split(DecArgs a) {
   constexpr int G = D / 8;   // lanes per cache row
   constexpr int R = 64 / G;  // rows per load instruction
-  constexpr int kUnroll = MQ >= 8 ? 2 : (MQ >= 4 ? 4 : 8);  // loads in flight per tensor
+  constexpr int kUnroll = MQ >= 8 ? 4 : (MQ >= 4 ? 8 : 16);  // loads in flight per tensor
   constexpr int kBlock = kUnroll * R;                        // rows per wave per block
   constexpr float kNegInf = -__builtin_huge_valf();
   static_assert(MQ >= 1 && MQ <= kMaxQ, "query rows");

@@ -216,7 +216,7 @@ def test_decode_workspace_sizes(lib):
     assert fa.fa2_decode_workspace_bytes(1, 1, 1, 16, 64) == 0
     assert fa.fa2_decode_workspace_bytes(1, 1, 1, 4096, 64) == 16 * 1 * 1 * 65 * 4
     assert fa.fa2_decode_workspace_bytes(2, 4, 3, 4096, 128) == 16 * 8 * 3 * 129 * 4
-    assert fa.fa2_decode_workspace_bytes(8, 32, 1, 16384, 128) == 4 * 256 * 129 * 4
+    assert fa.fa2_decode_workspace_bytes(8, 32, 1, 16384, 128) == 2 * 256 * 129 * 4
     assert fa.fa2_decode_workspace_bytes(64, 64, 1, 16384, 128) == 0  # 4096 heads fill the chip alone
     assert fa.fa2_decode_workspace_bytes(0, 4, 1, 4096, 128) == 0
     assert fa.fa2_decode_workspace_bytes(1, 1, 9, 16, 64) == -fa.FA2_ERR_SHAPE

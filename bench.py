@@ -29,6 +29,10 @@ if ROOT not in sys.path:
 
 PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth, published
+PEAK_FP8_MFMA_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
+# The fp8 forward runs half its products (Q K^T) at the fp8 peak and half (P V)
+# at the 16-bit peak: its ceiling is the time-weighted mix of the two.
+PEAK_FP8_QK_TFLOPS = 2.0 / (1.0 / PEAK_FP8_MFMA_TFLOPS + 1.0 / PEAK_MFMA_TFLOPS)
 DEFAULT_DECODE_WORKLOAD = "decode_b8h32_m1_n16384_d128"
 DEFAULT_WORKLOAD = "b1h32_n16384_d128_causal"
 PROFILES = os.path.join(ROOT, "profiles")
@@ -336,6 +340,9 @@ def main() -> int:
     ap.add_argument("--prefix", type=int, default=0, help="forward pass: keys below this are visible to every query")
     ap.add_argument("--documents", type=int, default=0,
                     help="forward pass: split each sequence into this many equal contiguous documents")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward pass with Q and K in fp8 (e4m3, per-head scales) and V, O in the workload's "
+                         "16-bit type (head dim 128)")
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "decode"), default="fwd",
                     help="time the forward pass (the headline), the gradient pass of the workload, or decode "
                          "against a key/value cache (a decode workload)")
@@ -366,8 +373,11 @@ def main() -> int:
         log(f"copied {n} bytes 5 times")
         return 0
 
-    if args.pass_ != "fwd" and (args.window is not None or args.prefix > 0 or args.documents > 0):
-        log("masks other than causal apply to the forward pass only")
+    if args.pass_ != "fwd" and (args.window is not None or args.prefix > 0 or args.documents > 0 or args.fp8):
+        log("masks other than causal, and fp8 inputs, apply to the forward pass only")
+        return 2
+    if args.fp8 and (args.window is not None or args.prefix > 0 or args.documents > 0):
+        log("the fp8 forward pass takes no mask or the causal mask")
         return 2
     if args.pass_ == "decode":
         return run_decode(args)
@@ -385,7 +395,27 @@ def main() -> int:
 
     masked = args.window is not None or args.prefix > 0 or args.documents > 0
     mask_cfg = None
-    if args.pass_ == "fwd" and masked:
+    peak = PEAK_MFMA_TFLOPS
+    if args.fp8:
+        if w.d != 128:
+            log("the fp8 forward pass serves head dim 128")
+            return 2
+        from exact_attention_11_amd.inputs import make_qkv_fp8
+        q8, k8, v16, dsq, dsk = make_qkv_fp8(w.B, w.H, w.N, w.d, q.dtype, w.dist, seed=0)
+        dq8, dk8, dv16, ddq, ddk = q8.cuda(), k8.cuda(), v16.cuda(), dsq.cuda(), dsk.cuda()
+        del dq, dk, dv
+
+        def step():
+            fa.forward_fp8(dq8, dk8, dv16, ddq, ddk, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        flop = flop_count(w.B, w.H, w.N, w.d, w.causal)
+        metric = ("attention fwd TFLOP/s with fp8 (e4m3) Q, K and 16-bit V, % of the MI355X MFMA ceiling for "
+                  "half fp8, half fp16/bf16 products")
+        peak = PEAK_FP8_QK_TFLOPS
+        # the oracle timing below runs on the real (descaled) inputs
+        q = q8.to(torch.float64) * dsq.to(torch.float64).reshape(w.B, w.H, 1, 1)
+        k = k8.to(torch.float64) * dsk.to(torch.float64).reshape(w.B, w.H, 1, 1)
+        v = v16
+    elif args.pass_ == "fwd" and masked:
         doc_len = -(-w.N // args.documents) if args.documents > 0 else 0
         seg = None
         if doc_len:
@@ -433,7 +463,7 @@ def main() -> int:
     log(f"{args.steps} steps: {ms_per_step:.4f} ms/step (events), launch avg {avg_launch_ms:.4f} ms, "
         f"min {min_ms:.4f} ms, wall {wall_ms:.4f} ms/step -> {value:.1f} TFLOP/s")
 
-    traffic = recorded_traffic(w.name) if args.pass_ == "fwd" and not masked else None
+    traffic = recorded_traffic(w.name) if args.pass_ == "fwd" and not masked and not args.fp8 else None
     result = {
         "metric": metric,
         "value": round(value, 3),
@@ -446,14 +476,14 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": f"fp8-e4m3 QK, {w.dtype} PV" if args.fp8 else w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "pass": args.pass_, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "config": {"workload": w.name, "pass": args.pass_, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "fp8": args.fp8,
                    "causal": w.causal, "mask": mask_cfg, "inputs": w.dist, "flop_per_step": flop,
                    "kernel_source_digest": kernel_source_digest(
                        KERNEL_SOURCES if args.pass_ == "fwd" else BWD_KERNEL_SOURCES)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
         "cpu_baseline": None,
     }

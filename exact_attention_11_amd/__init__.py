@@ -40,7 +40,7 @@ FA2_ERR_MASK = 10
 FA2_ERR_WORKSPACE = 11
 
 # Every symbol include/fa2.h declares.
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_bwd", "fa2_decode", "fa2_decode_workspace_bytes",
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_fwd_fp8", "fa2_bwd", "fa2_decode", "fa2_decode_workspace_bytes",
                     "fa2_status_str", "fa2_last_hip_error")
 DECODE_MAX_QUERIES = 8
 
@@ -86,6 +86,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                             ctypes.c_float, ctypes.c_int, vp]
     lib.fa2_bwd.restype = ctypes.c_int
+    lib.fa2_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp, vp,
+                                ctypes.c_int, vp]
+    lib.fa2_fwd_fp8.restype = ctypes.c_int
     lib.fa2_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                ctypes.c_int, vp, i64, vp]
     lib.fa2_decode.restype = ctypes.c_int
@@ -119,6 +122,13 @@ def fa2_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, delta: int, dq:
     """Direct call of the gradient entry point with raw device addresses; returns the status."""
     return load_library().fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, int(causal),
                                   float(scale), int(dtype), stream)
+
+
+def fa2_fwd_fp8(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, causal: int,
+                scale: float, descale_q: int | None, descale_k: int | None, dtype: int, stream: int) -> int:
+    """Direct call of the fp8 forward entry point with raw device addresses; returns the status."""
+    return load_library().fa2_fwd_fp8(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), descale_q, descale_k,
+                                      int(dtype), stream)
 
 
 def fa2_decode(q: int, k: int, v: int, seqlens: int | None, o: int, lse: int, B: int, H: int, Mq: int, Nk: int,
@@ -308,3 +318,46 @@ def decode(q, k, v, seqlens=None, causal: bool = False, scale: float | None = No
     if rc != FA2_OK:
         raise Fa2Error(rc, fa2_status_str(rc), "fa2_decode")
     return out, lse
+
+
+def forward_fp8(q8, k8, v, descale_q=None, descale_k=None, causal: bool = False, scale: float | None = None,
+                out=None, lse=None, stream=None):
+    """Attention forward with Q and K in fp8 (``torch.float8_e4m3fn``, [B, H, N,
+    128]) and V in fp16 or bf16.  The real inputs are ``q8 * descale_q[b*H + h]``
+    and ``k8 * descale_k[b*H + h]`` (``descale_*``: float32 [B*H] device tensors,
+    or None for ones).  Returns ``(o, lse)`` with ``o`` in V's dtype."""
+    import torch
+
+    if not (q8.shape == k8.shape == v.shape) or q8.dim() != 4:
+        raise ValueError("q8, k8, v must share one [B, H, N, d] shape")
+    if q8.dtype != torch.float8_e4m3fn or k8.dtype != torch.float8_e4m3fn:
+        raise TypeError("q8 and k8 must be torch.float8_e4m3fn")
+    code = _dtype_code(v)
+    ts = (q8, k8, v)
+    if any(not t.is_cuda or t.device != v.device for t in ts) or any(not t.is_contiguous() for t in ts):
+        raise ValueError("q8, k8, v must be contiguous tensors on one GPU")
+    B, H, N, d = v.shape
+    ptrs = []
+    for ds in (descale_q, descale_k):
+        if ds is None:
+            ptrs.append(None)
+            continue
+        if ds.shape != (B * H,) or ds.dtype != torch.float32 or not ds.is_contiguous() or ds.device != v.device:
+            raise ValueError("descales must be contiguous float32 [B*H] tensors on the inputs' device")
+        ptrs.append(ds.data_ptr())
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(v) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=v.device) if lse is None else lse
+    if out.shape != v.shape or out.dtype != v.dtype or not out.is_contiguous() or out.device != v.device:
+        raise ValueError("out must be a contiguous tensor like v")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != v.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on the inputs' device")
+    with torch.cuda.device(v.device):
+        s = stream if stream is not None else torch.cuda.current_stream(v.device)
+        rc = fa2_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                         int(bool(causal)), float(scale), ptrs[0], ptrs[1], code, s.cuda_stream)
+    if rc != FA2_OK:
+        raise Fa2Error(rc, fa2_status_str(rc), "fa2_fwd_fp8")
+    return out, lse
+

@@ -290,6 +290,8 @@ int fa2_fwd_masked(const void* q, const void* k, const void* v, void* o, float* 
   args.H = (int)H;
   args.seg = m.segment_ids;
   args.grow = mode == fa2::kMaskGeneral && wl < 0 && wr >= 0;
+  args.descale_q = nullptr;
+  args.descale_k = nullptr;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_d<0>(args, d, mode, s) : launch_d<1>(args, d, mode, s);
@@ -436,6 +438,71 @@ int fa2_decode(const void* q, const void* k, const void* v, const int32_t* seqle
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_decode_d<0>(args, d, s) : launch_decode_d<1>(args, d, s);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA2_ERR_LAUNCH;
+  }
+  return FA2_OK;
+}
+
+int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+                int64_t d, int causal, float scale, const float* descale_q, const float* descale_k, int dtype,
+                void* stream) {
+  g_last_hip_error = 0;
+  // ---- argument checks: no HIP call before they all pass -------------------
+  if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
+  if (d != 128) return FA2_ERR_HEADDIM;
+  if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
+  const float c2 = (float)((double)scale * 1.4426950408889634074);
+  if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) return FA2_OK;
+  if (N > (int64_t)INT32_MAX - 65536) return FA2_ERR_SHAPE;
+  if (B > INT32_MAX || H > INT32_MAX) return FA2_ERR_SHAPE;
+  const int64_t bh = B * H;
+  const int64_t n_qtiles = (N + fa2::w8::kBr - 1) / fa2::w8::kBr;
+  if (bh > (int64_t)INT32_MAX / n_qtiles) return FA2_ERR_SHAPE;
+  if (bh > (INT64_MAX / 4) / (N * d)) return FA2_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_NULLPTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA2_ERR_ALIGN;
+  if (((uintptr_t)descale_q | (uintptr_t)descale_k) & 3) return FA2_ERR_ALIGN;
+  const uint64_t b8 = (uint64_t)(bh * N * d), b16 = 2 * b8, lb = (uint64_t)(bh * N) * 4, sb = (uint64_t)bh * 4;
+  const void* in[5] = {q, k, v, descale_q, descale_k};
+  const uint64_t in_n[5] = {b8, b8, b16, descale_q ? sb : 0, descale_k ? sb : 0};
+  for (int j = 0; j < 5; ++j) {
+    if (in_n[j] == 0) continue;
+    if (overlaps(o, b16, in[j], in_n[j]) || overlaps(lse, lb, in[j], in_n[j])) return FA2_ERR_ALIAS;
+  }
+  if (overlaps(o, b16, lse, lb)) return FA2_ERR_ALIAS;
+
+  // ---- device ---------------------------------------------------------------
+  const int dev_status = check_device();
+  if (dev_status != FA2_OK) return dev_status;
+
+  fa2::FwdArgs args;
+  args.q = (const uint16_t*)q;  // e4m3 bytes, addressed as such by the fp8 instances
+  args.k = (const uint16_t*)k;
+  args.v = (const uint16_t*)v;
+  args.o = (uint16_t*)o;
+  args.lse = lse;
+  args.N = (int)N;
+  args.n_qtiles = (int)n_qtiles;
+  args.n_wg = (int)(bh * n_qtiles);
+  args.c2 = c2;
+  args.wl = -1;
+  args.wr = causal ? 0 : -1;
+  args.prefix = 0;
+  args.H = (int)H;
+  args.seg = nullptr;
+  args.grow = 0;
+  args.descale_q = descale_q;
+  args.descale_k = descale_k;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == FA2_DTYPE_FP16)
+    e = causal ? launch<fa2::kFp8Fp16, 128, fa2::kMaskCausal>(args, s) : launch<fa2::kFp8Fp16, 128, fa2::kMaskNone>(args, s);
+  else
+    e = causal ? launch<fa2::kFp8Bf16, 128, fa2::kMaskCausal>(args, s) : launch<fa2::kFp8Bf16, 128, fa2::kMaskNone>(args, s);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FA2_ERR_LAUNCH;

@@ -16,6 +16,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define FA2_LDS __attribute__((address_space(3)))
 
@@ -48,7 +49,18 @@ struct FwdArgs {
   int H;            // heads per batch: batch b = (b*H + h) / H
   const int* seg;   // [B, N] segment ids, or nullptr
   int grow;         // general mask whose tile cost grows with the query tile (order those heaviest first)
+  // fp8 instances: per-(batch, head) factors that turn the stored e4m3 values
+  // of Q and K into real ones (nullptr: 1).
+  const float* descale_q;
+  const float* descale_k;
 };
+
+// Element types of the forward kernels: Q, K, V and O in fp16 or bf16, or Q and
+// K in fp8 (OCP e4m3) with V and O in fp16 or bf16.
+constexpr int kFp16 = 0;
+constexpr int kBf16 = 1;
+constexpr int kFp8Fp16 = 2;
+constexpr int kFp8Bf16 = 3;
 
 // Mask modes of the forward kernels.
 constexpr int kMaskNone = 0;
@@ -78,6 +90,17 @@ template <> struct Elem<1> {  // bf16
     return __builtin_bit_cast(uint32_t, h);
   }
 };
+
+// S^T = K Q^T over 64 k-elements of fp8 (OCP e4m3) K and Q, fp32 accumulation:
+// v_mfma_f32_32x32x64_f8f6f4 with both operand formats e4m3 (format code 0) and
+// no block scales.  Lane l holds 32 consecutive k-bytes of row l % 32 of its
+// operand; which 32 (the lane half) only has to agree between the two
+// operands.  A template, like Elem's products, so that the host pass of the
+// kernels that call it (which only emits their launch stubs) never checks the
+// gfx950-only builtin.
+template <int kFormat = 0> __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kFormat, kFormat, 0, 0, 0, 0);
+}
 
 // One global_load_lds_dwordx4: every lane copies 16 bytes from its own global
 // address to lds_base + 16 * lane (lds_base is wave-uniform and goes in M0).

@@ -50,6 +50,8 @@
 //    of heads (L2 reuse of K/V); causal query tiles go heaviest first.
 #pragma once
 
+#include <type_traits>
+
 #include "fa2_common.h"
 
 namespace fa2 {
@@ -90,20 +92,31 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   constexpr bool kCausal = kMask == kMaskCausal;
   constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
   constexpr bool kSeg = kMask == kMaskSegments;
-  typedef Elem<kDType> E;
+  // fp8 instances: S = K Q^T on the fp8 MFMA from e4m3 Q and K; V, P and O stay
+  // 16-bit, so P.V and everything after the scores are those of the 16-bit
+  // instances.
+  constexpr bool kQK8 = kDType == kFp8Fp16 || kDType == kFp8Bf16;
+  typedef Elem<kDType & 1> E;  // P.V and the output
   typedef typename E::V8 V8;
-  constexpr int CPR = D / 8;                          // 16-byte chunks per K/V row
-  constexpr int KS = D / 16;                          // k-steps of S = K Q^T
+  typedef std::conditional_t<kQK8, i32x8, V8> QF;  // one S operand fragment of Q
+  constexpr int kEbK = kQK8 ? 1 : 2;                 // bytes per element of Q and K
+  constexpr int CPR = D / 8;                          // 16-byte chunks per V row
+  constexpr int CPRK = D * kEbK / 16;                 // 16-byte chunks per K row
+  constexpr int KS = kQK8 ? D / 64 : D / 16;          // k-steps of S = K Q^T
   constexpr int DB = D / 32;                          // 32-wide output column blocks
-  constexpr int kTile = kBc * D;                      // elements of one K, V or V^T tile
-  constexpr int kLoads = kBc * CPR / (64 * kWaves);   // copy instructions per wave per tensor
-  constexpr int kRowStep = 4 * 16 * kWaves / CPR;     // rows covered by one instruction of all waves
+  constexpr int kTile = kBc * D;                      // elements of one K, V or V^T slot
+  constexpr int kLoads = kBc * CPR / (64 * kWaves);   // copy instructions per wave per V tile
+  constexpr int kLoadsK = kBc * CPRK / (64 * kWaves); // ... per K tile
+  constexpr int kRowStep = 4 * 16 * kWaves / CPR;     // rows covered by one instruction of all waves (V)
+  constexpr int kRowStepK = 4 * 16 * kWaves / CPRK;   // ... (K)
   constexpr float kNegInf = -__builtin_huge_valf();
   static_assert(D == 64 || D == 128, "head dim");
+  static_assert(!kQK8 || D == 128, "fp8 instances serve head dim 128");
   static_assert(kLoads >= 1 && kLoads * 64 * kWaves == kBc * CPR, "tile copy split");
+  static_assert(kLoadsK >= 1 && kLoadsK * 64 * kWaves == kBc * CPRK, "tile copy split");
   // Copy instructions per wave per tile: K and V, plus the keys' segment ids
   // under segment ids (issued by every wave, so the counts stay uniform).
-  constexpr int kTileLoads = 2 * kLoads + (kSeg ? 1 : 0);
+  constexpr int kTileLoads = kLoadsK + kLoads + (kSeg ? 1 : 0);
   constexpr int kSegSlots = 4;  // segment ids of tiles st..st+2 stay readable while group 1 reads st-1
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem_[(kKSlots + kVSlots + kTSlots) * kTile];
@@ -127,8 +140,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   const int q_row0 = qtile * kBr + wave * 32;
   const int my_q = q_row0 + col;
   const int64_t head_off = (int64_t)bh * N * D;
-  const uint16_t* __restrict__ kh = a.k + head_off;
+  const char* __restrict__ kh = (const char*)a.k + head_off * kEbK;  // K of this head, bytes
   const uint16_t* __restrict__ vh = a.v + head_off;
+  // Score multiplier in log2 units (the fp8 instances fold in the descales).
+  float c2 = a.c2;
+  if constexpr (kQK8) {
+    if (a.descale_q) c2 *= a.descale_q[bh];
+    if (a.descale_k) c2 *= a.descale_k[bh];
+  }
 
   // Copy layout: instruction t of this wave fills the 1 KB at q = t*kWaves +
   // wave, i.e. blocks 4q..4q+3: rows 16*(4q / CPR) + 0..15 of chunks
@@ -138,10 +157,13 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   // wave-uniform base.
   const int cch = (4 * wave) % CPR + (lane >> 4);     // chunk this lane copies
   const int crow = 16 * ((4 * wave) / CPR);          // first row of its block (t = 0)
-  const int kr = crow + (lane & 15);                  // K: LDS row; holds key sigma(kr)
   const int vr = crow + ((lane & 15) ^ (4 * (cch & 3)));  // V: row that lands in slot lane & 15
-  const uint32_t voffK = (uint32_t)((sigma(kr) * D + cch * 8) * 2);
   const uint32_t voffV = (uint32_t)((vr * D + cch * 8) * 2);
+  // The same for K with its own row length (CPRK chunks); LDS row krK holds
+  // key sigma(krK).
+  const int cchK = (4 * wave) % CPRK + (lane >> 4);
+  const int krK = 16 * ((4 * wave) / CPRK) + (lane & 15);
+  const uint32_t voffK = (uint32_t)(sigma(krK) * D * kEbK + cchK * 16);
 
   // Key tiles: step st of the loop visits tile tile_of(st), st < nt.  Without a
   // general mask those are tiles 0 .. nt-1 (under the causal mask up to the
@@ -192,20 +214,32 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
     FA2_LDS uint16_t* dk = sK + slot * kTile;
     FA2_LDS uint16_t* dv = sVs + slot * kTile;
     if (kv0 + kBc <= N) {
-      const char* kb = (const char*)(kh + (int64_t)kv0 * D);
+      const char* kb = kh + (int64_t)kv0 * D * kEbK;
       const char* vb = (const char*)(vh + (int64_t)kv0 * D);
+      if constexpr (kLoadsK == kLoads) {
 #pragma unroll
-      for (int t = 0; t < kLoads; ++t) {
-        dma16_sbase(kb + t * kRowStep * D * 2, voffK, dk + (t * kWaves + wave) * 64 * 8);
-        dma16_sbase(vb + t * kRowStep * D * 2, voffV, dv + (t * kWaves + wave) * 64 * 8);
+        for (int t = 0; t < kLoads; ++t) {
+          dma16_sbase(kb + t * kRowStepK * D * kEbK, voffK, dk + (t * kWaves + wave) * 64 * 8);
+          dma16_sbase(vb + t * kRowStep * D * 2, voffV, dv + (t * kWaves + wave) * 64 * 8);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kLoadsK; ++t)
+          dma16_sbase(kb + t * kRowStepK * D * kEbK, voffK, dk + (t * kWaves + wave) * 64 * 8);
+#pragma unroll
+        for (int t = 0; t < kLoads; ++t)
+          dma16_sbase(vb + t * kRowStep * D * 2, voffV, dv + (t * kWaves + wave) * 64 * 8);
       }
     } else {
       // Ragged last tile: rows past N re-read row N-1 (their scores are masked).
 #pragma unroll
+      for (int t = 0; t < kLoadsK; ++t) {
+        const int gk = min(kv0 + sigma(krK + t * kRowStepK), N - 1);
+        dma16(kh + (int64_t)gk * D * kEbK + cchK * 16, dk + (t * kWaves + wave) * 64 * 8);
+      }
+#pragma unroll
       for (int t = 0; t < kLoads; ++t) {
-        const int gk = min(kv0 + sigma(kr + t * kRowStep), N - 1);
         const int gv = min(kv0 + vr + t * kRowStep, N - 1);
-        dma16(kh + (int64_t)gk * D + cch * 8, dk + (t * kWaves + wave) * 64 * 8);
         dma16(vh + (int64_t)gv * D + cch * 8, dv + (t * kWaves + wave) * 64 * 8);
       }
     }
@@ -226,8 +260,20 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
 
   // Q fragments (B operand of S^T = K Q^T), kept in registers for the whole
   // loop.  Consumed here so the compiler's wait for them stays out of the loop.
-  V8 qf[KS];
-  {
+  QF qf[KS];
+  if constexpr (kQK8) {
+    // Lane (hl, col): bytes 64 ks + 32 hl .. + 31 of its query row.
+    const char* qp = (const char*)a.q + head_off + (int64_t)min(my_q, N - 1) * D + 32 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 lo = *(const u32x4*)(qp + 64 * ks);
+      const u32x4 hi = *(const u32x4*)(qp + 64 * ks + 16);
+      // (128-bit operands: the host pass checks the constraint against the host
+      // target, where a 256-bit "v" operand is not valid.)
+      asm volatile("" ::"v"(lo), "v"(hi));
+      qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  } else {
     const uint16_t* qp = a.q + head_off + (int64_t)min(my_q, N - 1) * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(qp + 16 * ks));
@@ -267,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
 
   // Operand addresses: lane (hl, col) reads row 32*kb + col, chunk 2*ks + hl of
   // K, and column 32*db + col, chunk 2*c + hl of V^T.
-  const uint32_t kaddr0 = k_byte<CPR>(col, hl);
+  const uint32_t kaddr0 = k_byte<CPRK>(col, kQK8 ? 2 * hl : hl);
   const uint32_t taddr0 = k_byte<kBc / 8>(col, hl);
 
   // The products of one phase run as one pipeline over their operand
@@ -286,14 +332,22 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   // (prefetch): the barrier's wait then covers the load latency.
   constexpr int kPipe = 4;
   constexpr int kNpv = (kBc / 16) * DB;  // P.V fragments
-  constexpr int kNs = 2 * KS;            // S fragments: f -> (ks = f / 2, kb = f % 2)
+  // S fragments: f -> (ks = f / 2, kb = f % 2); an fp8 S operand is two
+  // 16-byte halves, loaded as consecutive fragments 2f and 2f + 1.
+  constexpr int kNs = kQK8 ? 4 * KS : 2 * KS;
   static_assert(kPipe <= 2 * DB, "prefetched fragments must lie in keys 32-63");
   auto pv_c = [](int f) constexpr { return (f / DB + 2) % (kBc / 16); };
   V8 fr[kPipe];
   auto load_op = [&](uint32_t tbase, uint32_t kbase, int i) __attribute__((always_inline)) {
     uint32_t ad;
-    if (i < kNpv) ad = tbase + (uint32_t)((((i % DB) * 2 * (kBc / 8)) + 2 * pv_c(i)) << 8);
-    else ad = kbase + (uint32_t)(((((i - kNpv) & 1) * 2 * CPR) + 2 * ((i - kNpv) >> 1)) << 8);
+    if (i < kNpv) {
+      ad = tbase + (uint32_t)((((i % DB) * 2 * (kBc / 8)) + 2 * pv_c(i)) << 8);
+    } else if constexpr (kQK8) {
+      const int f = (i - kNpv) >> 1, h = (i - kNpv) & 1;  // lane reads chunk 4 ks + 2 hl + h of row 32 kb + col
+      ad = kbase + (uint32_t)((((f & 1) * 2 * CPRK) + 4 * (f >> 1) + h) << 8);
+    } else {
+      ad = kbase + (uint32_t)(((((i - kNpv) & 1) * 2 * CPRK) + 2 * ((i - kNpv) >> 1)) << 8);
+    }
     return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(size_t)ad);
   };
   auto tslot_base = [&](int tslot) __attribute__((always_inline)) {
@@ -332,11 +386,24 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
         const u32x4 bw = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1], pk[c >> 1][4 * (c & 1) + 2],
                           pk[c >> 1][4 * (c & 1) + 3]};
         o[i % DB] = E::mfma(fr[i % kPipe], __builtin_bit_cast(V8, bw), o[i % DB]);
+      } else if constexpr (kQK8) {
+        // An fp8 MFMA takes the fragment pair (i - 1, i): issue it on the second
+        // half, and reload the pair's slots only then.
+        const int k = i - kNpv;
+        if (k & 1) {
+          const u32x4 lo = __builtin_bit_cast(u32x4, fr[(i - 1) % kPipe]);
+          const u32x4 hi = __builtin_bit_cast(u32x4, fr[i % kPipe]);
+          const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          s[(k >> 1) & 1] = mfma_fp8(ka, qf[k >> 2], s[(k >> 1) & 1]);
+          if (i - 1 + kPipe < kNpv + kNs) fr[(i - 1) % kPipe] = load_op(tbase, kbase, i - 1 + kPipe);
+        }
       } else {
         const int k = i - kNpv;
         s[k & 1] = E::mfma(fr[i % kPipe], qf[k >> 1], s[k & 1]);
       }
-      if (i + kPipe < kNpv + kNs) fr[i % kPipe] = load_op(tbase, kbase, i + kPipe);
+      if (i + kPipe < kNpv + kNs && !(kQK8 && i >= kNpv && ((i - kNpv) & 1) == 0))
+        fr[i % kPipe] = load_op(tbase, kbase, i + kPipe);
       if (i == 6 && copy_tile >= 0) {
         __builtin_amdgcn_sched_barrier(0);
         issue_tile(copy_tile, copy_slot);
@@ -398,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
                         (k1 < a.prefix || ((a.wl < 0 || kv0 >= qb - a.wl) && (a.wr < 0 || k1 <= qa + a.wr)));
       need_mask = !full;
     }
-    float mul = a.c2;
+    float mul = c2;
     if (kGeneral && need_mask) {
       // Key of element (kb, r) = kv0 + 8*hl + off with a constant off.
       const int base = kv0 + 8 * hl;
@@ -407,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
       const int lo_w = a.wl < 0 ? INT32_MIN / 2 : my_q - a.wl - base;
       const int hi_w = a.wr < 0 ? INT32_MAX / 2 : my_q + a.wr - base;
       const FA2_LDS int* sk = sSeg + (step % kSegSlots) * kBc + 8 * hl;
-      const bool pos = a.c2 > 0.f;
+      const bool pos = c2 > 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -423,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
             const int off = 32 * kb + 16 * h8 + i;
             bool ok = off < lim_n && (off < lim_p || (off >= lo_w && off <= hi_w));
             if (kSeg && !seg_all) ok = ok && (int)sg[i >> 2][i & 3] == seg_q;
-            const float t = pos ? s[kb][r] : s[kb][r] * a.c2;
+            const float t = pos ? s[kb][r] : s[kb][r] * c2;
             s[kb][r] = ok ? t : kNegInf;
           }
         }
@@ -435,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
       const int base = kv0 + 8 * hl;
       int lim = N - base;
       if (kCausal) lim = min(lim, my_q + 1 - base);
-      if (a.c2 > 0.f) {
+      if (c2 > 0.f) {
         // -inf times a positive multiplier stays -inf: mask the raw scores.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -451,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int off = 32 * kb + 16 * (r >> 3) + (r & 7);
-            const float t = s[kb][r] * a.c2;
+            const float t = s[kb][r] * c2;
             s[kb][r] = off < lim ? t : kNegInf;
           }
         mul = 1.f;

@@ -146,3 +146,40 @@ def decode_workload_inputs(w: DecodeWorkload, seed: int = 0):
     q, k, v = make_decode_inputs(w.B, w.H, w.Mq, w.Nk, w.d, w.torch_dtype, seed)
     return q, k, v, decode_lengths(w.B, w.Nk, w.lengths, seed)
 
+
+FP8_E4M3_MAX = 448.0  # largest finite OCP e4m3 value
+
+
+def make_qkv_fp8(B: int, H: int, N: int, d: int, v_dtype, dist: str = "normal", seed: int = 0):
+    """Q and K quantised to OCP e4m3 with one scale per (batch, head), V in
+    ``v_dtype``: the values of ``make_qkv(B, H, N, d, float32-like, dist, seed)``
+    (drawn in fp32 in the order Q, K, V), with Q[b, h] divided by
+    descale_q[b*H + h] = max |Q[b, h]| / 448 and cast to e4m3 by torch (round
+    to nearest even), likewise K.  Returns host tensors
+    ``(q8, k8, v, descale_q, descale_k)``; q8 * descale_q and k8 * descale_k are
+    the real inputs."""
+    if isinstance(v_dtype, str):
+        v_dtype = torch.float16 if v_dtype == "fp16" else torch.bfloat16
+    g = torch.Generator("cpu").manual_seed(seed)
+    shape = (B, H, N, d)
+    if dist == "normal":
+        q = torch.randn(shape, generator=g, dtype=torch.float32)
+        k = torch.randn(shape, generator=g, dtype=torch.float32)
+        v = torch.randn(shape, generator=g, dtype=torch.float32)
+    elif dist == "peaky":
+        q = torch.randn(shape, generator=g, dtype=torch.float32) * 3.0
+        k = torch.randn(shape, generator=g, dtype=torch.float32) * 3.0
+        v = torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0
+    else:
+        raise ValueError(dist)
+
+    def quant(x):
+        amax = x.abs().amax(dim=(2, 3)).clamp_min(1e-30)           # [B, H]
+        ds = (amax / FP8_E4M3_MAX).to(torch.float32)
+        x8 = (x / ds[:, :, None, None]).clamp(-FP8_E4M3_MAX, FP8_E4M3_MAX).to(torch.float8_e4m3fn)
+        return x8, ds.reshape(-1).contiguous()
+
+    q8, dq = quant(q)
+    k8, dk = quant(k)
+    return q8, k8, v.to(v_dtype), dq, dk
+

@@ -206,6 +206,33 @@ int fa2_decode(const void* q, const void* k, const void* v, const int32_t* seqle
                int causal, float scale, int dtype, void* workspace, int64_t workspace_bytes,
                void* stream);
 
+/*
+ * fa2_fwd_fp8 -- fa2_fwd with Q and K stored in fp8 (OCP e4m3, one byte per
+ * element) and V, O in fp16 or bf16 (`dtype`): enqueue on `stream` and return
+ * without waiting.  The real inputs are q_real = descale_q[b*H + h] * q and
+ * k_real = descale_k[b*H + h] * k, and the result is fa2_fwd's on them:
+ *
+ *   O = softmax(scale * q_real k_real^T [+ causal mask]) V,   L = log sum exp(...)
+ *
+ *  - Lower-precision inputs for speed, with the extra rounding error kept small,
+ *    is the FP8 idea of "Flash Attention: Memory-Efficient Attention at Scale",
+ *    section "Flash Attention 3".  Here the products q.k run on the fp8 MFMA
+ *    and are exact in fp32 for the stored values; the weights P and the P.V
+ *    product stay 16-bit, so the only rounding beyond fa2_fwd's is the caller's
+ *    own quantisation of Q and K.
+ *
+ * q, k       : [B, H, N, 128] e4m3 bytes, device, read only.
+ * v          : [B, H, N, 128] `dtype`, device, read only.
+ * o, lse     : as for fa2_fwd.
+ * descale_q, descale_k : [B*H] float32 device arrays (read only, 4-byte
+ *              aligned), or NULL for all ones.
+ * Other arguments, layout rules, errors and the empty-problem rule as for
+ * fa2_fwd; d must be 128 (FA2_ERR_HEADDIM otherwise).
+ */
+int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                const float* descale_q, const float* descale_k, int dtype, void* stream);
+
 /* Bytes of workspace fa2_decode needs for these sizes (0: none), or minus a
  * fa2_status code for sizes fa2_decode would reject.  Host only; no HIP call. */
 int64_t fa2_decode_workspace_bytes(int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d);
@@ -213,8 +240,8 @@ int64_t fa2_decode_workspace_bytes(int64_t B, int64_t H, int64_t Mq, int64_t Nk,
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char* fa2_status_str(int status);
 
-/* Last HIP error code seen by a failing fa2_fwd, fa2_fwd_masked, fa2_bwd or
- * fa2_decode call on this thread (0 if none); useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
+/* Last HIP error code seen by a failing fa2_fwd, fa2_fwd_masked, fa2_fwd_fp8,
+ * fa2_bwd or fa2_decode call on this thread (0 if none); useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
 int fa2_last_hip_error(void);
 
 #ifdef __cplusplus

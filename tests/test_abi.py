@@ -270,3 +270,50 @@ def test_python_decode_rejects_bad_tensors(lib):
     with pytest.raises(TypeError):
         fa.decode(q.float(), kv.float(), kv.float())
 
+
+# --- fa2_fwd_fp8 -------------------------------------------------------------------
+
+DQS, DKS = 0xD0000000, 0xE0000000
+
+
+def _fp8(B=1, H=1, N=16, d=128, causal=0, scale=0.125, dtype=0, q=Q, k=K, v=V, o=O, lse=L, dq=DQS, dk=DKS):
+    return fa.fa2_fwd_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, dq, dk, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(B=-1), fa.FA2_ERR_SHAPE), (dict(N=2 ** 31), fa.FA2_ERR_SHAPE),
+    (dict(d=64), fa.FA2_ERR_HEADDIM), (dict(d=256), fa.FA2_ERR_HEADDIM),
+    (dict(dtype=2), fa.FA2_ERR_DTYPE), (dict(scale=math.inf), fa.FA2_ERR_SCALE),
+    (dict(q=0), fa.FA2_ERR_NULLPTR), (dict(v=0), fa.FA2_ERR_NULLPTR), (dict(lse=0), fa.FA2_ERR_NULLPTR),
+    (dict(k=K + 8), fa.FA2_ERR_ALIGN), (dict(dq=DQS + 2), fa.FA2_ERR_ALIGN),
+    (dict(o=Q), fa.FA2_ERR_ALIAS), (dict(o=V + 256), fa.FA2_ERR_ALIAS), (dict(lse=DKS), fa.FA2_ERR_ALIAS),
+    (dict(lse=O + 16), fa.FA2_ERR_ALIAS),
+])
+def test_fp8_argument_checks(lib, kwargs, code):
+    assert _fp8(**kwargs) == code
+
+
+def test_fp8_empty_problem_is_a_no_op(lib):
+    assert _fp8(B=0) == fa.FA2_OK
+    assert _fp8(N=0, q=0, k=0) == fa.FA2_OK
+
+
+def test_fp8_valid_call_without_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    for dtype in (0, 1):
+        for causal in (0, 1):
+            assert _fp8(dtype=dtype, causal=causal, N=4099) == fa.FA2_ERR_DEVICE
+    assert _fp8(dq=0, dk=0) == fa.FA2_ERR_DEVICE
+
+
+def test_python_fp8_forward_rejects_bad_tensors(lib):
+    import torch
+    q8 = torch.zeros(1, 1, 8, 128, dtype=torch.float8_e4m3fn)
+    v = torch.zeros(1, 1, 8, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.forward_fp8(q8, q8, v)  # host tensors
+    with pytest.raises(TypeError):
+        fa.forward_fp8(v, v, v)
+

@@ -204,6 +204,42 @@ def decode_bytes(w, lens) -> float:
     return kv + qo + w.B * w.H * w.Mq * 4
 
 
+def cpu_baseline_masked(w, q, k, v, window, prefix, seg, pairs_per_head, target_s: float = 12.0):
+    """Time the fp64 general-mask oracle on whole heads of the workload, one head
+    per host thread per call, until about ``target_s`` seconds have passed; the
+    rate counts 4 d FLOP per visible (query, key) pair, like the GPU line."""
+    import numpy as np
+
+    import oracle
+
+    threads = host_threads()
+    scale = float(np.float32(w.scale))
+    wl, wr = window if window is not None else (-1, -1)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, flop, secs = 0, 0.0, 0.0
+    while done < len(heads) and secs < target_s:
+        batch = heads[done:done + threads]
+        # one batch entry per head, each with its batch's segment ids
+        qs = np.stack([q[b, h].double().numpy() for b, h in batch])[:, None]
+        ks = np.stack([k[b, h].double().numpy() for b, h in batch])[:, None]
+        vs = np.stack([v[b, h].double().numpy() for b, h in batch])[:, None]
+        segs = None if seg is None else np.stack([seg[b] for b, _ in batch])
+        t0 = time.perf_counter()
+        oracle.attention_masked_f64(qs, ks, vs, scale, window_left=wl, window_right=wr, prefix=prefix,
+                                    segment_ids=segs, causal=w.causal, nthreads=threads)
+        secs += time.perf_counter() - t0
+        flop += 4.0 * w.d * pairs_per_head * len(batch)
+        done += len(batch)
+    return {
+        "value": flop / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} whole head(s) of {w.name} under the mask: {flop / 1e9:.1f} GFLOP of visible pairs in "
+                  f"{secs:.1f} s (fp64 general-mask oracle)",
+    }
+
+
 def cpu_baseline_decode(w, q, k, v, lens, target_s: float = 12.0):
     """Time the fp64 decode oracle on whole (batch, head) pairs, one pair per host
     thread per call (the oracle works a (batch, head) pair per thread), until
@@ -418,8 +454,10 @@ def main() -> int:
     elif args.pass_ == "fwd" and masked:
         doc_len = -(-w.N // args.documents) if args.documents > 0 else 0
         seg = None
+        seg_host = None
         if doc_len:
-            seg = (torch.arange(w.N, dtype=torch.int32) // doc_len).repeat(w.B, 1).contiguous().cuda()
+            seg_host = (torch.arange(w.N, dtype=torch.int32) // doc_len).repeat(w.B, 1).contiguous()
+            seg = seg_host.cuda()
         window = tuple(args.window) if args.window is not None else None
 
         def step():
@@ -490,7 +528,9 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the workload ...")
         if args.pass_ == "fwd" and masked:
-            result["cpu_baseline"] = None  # the row-sampled oracle covers the plain masks only
+            result["cpu_baseline"] = cpu_baseline_masked(w, q, k, v, window, args.prefix,
+                                                         None if seg_host is None else seg_host.numpy(),
+                                                         mask_cfg["visible_pairs_per_head"], args.cpu_seconds)
         elif args.pass_ == "fwd":
             result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
         else:

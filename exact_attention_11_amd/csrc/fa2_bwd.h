@@ -21,8 +21,9 @@
 //    o = p.v by the chain rule: dV = P^T dO, dP = dO V^T, dQ = scale dS K,
 //    dK = scale dS^T Q.
 //
-// gfx950 mapping.  Four wavefronts per workgroup (one per SIMD: the dK and dV
-// accumulators of 32 keys take 128 registers at d = 128, 256 at d = 256).
+// gfx950 mapping.  Four wavefronts per workgroup, one per SIMD, and two
+// workgroups per CU up to d = 128 (64 KB of LDS each), so that two wavefronts
+// share every SIMD and one's products overlap the other's elementwise work.
 // All products run on v_mfma_f32_32x32x16 with fp32 accumulation.
 //  * fa2_bwd_dkdv: wave w owns keys kw0 .. kw0+31 and keeps K and V of those
 //    keys in registers as the B operands of S = Q K^T and dP = dO V^T; the Q and
@@ -52,6 +53,14 @@ constexpr int kQTile = 64;               // fa2_bwd_dkdv: query rows per streame
 constexpr int kRowsPerWg = 32 * kWaves;  // fa2_bwd_dq: query rows per workgroup
 constexpr int kKTile = 64;               // fa2_bwd_dq: keys per streamed tile
 constexpr int kDeltaRows = 16;           // fa2_bwd_delta: rows per workgroup (16 lanes each)
+// Workgroups per CU each kernel is compiled for: two (two wavefronts per SIMD,
+// at most 256 registers each) up to d = 128, so that one workgroup's products
+// overlap the other's softmax gradient and memory waits; one at d = 256, where
+// the accumulators alone take 256 registers.  (fa2_bwd_dkdv at d = 128 then
+// spills a few of its K/V operand registers, and still runs faster than at one
+// workgroup per CU.)
+template <int D> constexpr int kDkdvWgPerCu = D <= 128 ? 2 : 1;
+template <int D> constexpr int kDqWgPerCu = D <= 128 ? 2 : 1;
 
 struct BwdArgs {
   const uint16_t* q;
@@ -94,21 +103,24 @@ template <int D> __device__ __forceinline__ uint32_t tile_byte(int row, int chun
 }
 
 // Copy R rows (r0.., clamped to N - 1) of a [N, D] head into an LDS tile; each
-// instruction of a wave fills 64 consecutive 16-byte slots.
+// instruction of a wave fills 64 consecutive 16-byte slots.  Addressed as the
+// wave-uniform row r0 plus a 32-bit per-lane offset, so that no per-lane 64-bit
+// address stays live across the kernel's loop.
 template <int D, int R>
 __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2_LDS uint16_t* dst, int r0, int N,
                                           int wave, int lane) {
   constexpr int CPR = D / 8;
   constexpr int kPer = R * CPR / (64 * kWaves);
   static_assert(kPer * 64 * kWaves == R * CPR, "tile copy split");
+  const uint16_t* base = head + (int64_t)r0 * D;
+  const int last = N - 1 - r0;  // rows past it re-read row N - 1
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     const int s0 = (t * kWaves + wave) * 64;
     const int s = s0 + lane;
     const int row = s / CPR;
     const int ch = (s % CPR) ^ swz<D>(row);
-    const int grow = min(r0 + row, N - 1);
-    dma16(head + (int64_t)grow * D + ch * 8, dst + s0 * 8);
+    dma16_sbase(base, (uint32_t)(min(row, last) * D * 2 + ch * 16), dst + s0 * 8);
   }
 }
 
@@ -149,7 +161,7 @@ __global__ __launch_bounds__(256) void fa2_bwd_delta(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK and dV of kKeysPerWg keys of one head; query tiles stream through LDS.
 template <int kDType, int D, bool kCausal>
-__global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArgs a) {
   typedef Elem<kDType> E;
   typedef typename E::V8 V8;
   constexpr int KS = D / 16;  // k-steps of S = Q K^T over the head dim
@@ -322,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ of kRowsPerWg query rows of one head; key/value tiles stream through LDS.
 template <int kDType, int D, bool kCausal>
-__global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a) {
   typedef Elem<kDType> E;
   typedef typename E::V8 V8;
   constexpr int KS = D / 16;

@@ -114,10 +114,15 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2
   static_assert(kPer * 64 * kWaves == R * CPR, "tile copy split");
   const uint16_t* base = head + (int64_t)r0 * D;
   const int last = N - 1 - r0;  // rows past it re-read row N - 1
+  // From d = 128 on, the lane index as a value the compiler cannot see
+  // through: the per-copy offsets below are then formed here, at each call,
+  // instead of being kept (or spilled) across the caller's loop.  (At d = 64
+  // the kernels have registers to spare and keep them.)
+  const int ln = D >= 128 ? (int)opaque_vgpr((uint32_t)lane) : lane;
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     const int s0 = (t * kWaves + wave) * 64;
-    const int s = s0 + lane;
+    const int s = s0 + ln;
     const int row = s / CPR;
     const int ch = (s % CPR) ^ swz<D>(row);
     dma16_sbase(base, (uint32_t)(min(row, last) * D * 2 + ch * 16), dst + s0 * 8);
@@ -166,13 +171,22 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
   typedef typename E::V8 V8;
   constexpr int KS = D / 16;  // k-steps of S = Q K^T over the head dim
   constexpr int DB = D / 32;  // 32-wide blocks of the head dim
-  constexpr int kTile = kQTile * D;
+  // At d = 256 the dK/dV accumulators alone take 256 registers: V (the B
+  // operand of dP = dO V^T) is read from an LDS copy of the workgroup's keys
+  // instead of being held in 64 more, and Q and dO stream in 32-row tiles so
+  // that the copy fits.
+  constexpr bool kVLds = D == 256;
+  constexpr int QT = kVLds ? 32 : kQTile;  // query rows per streamed tile
+  constexpr int kTile = QT * D;
+  constexpr int kStat = 64;  // floats per L or D row of the stat buffers (one copy of 64 lanes)
 
-  // [buffer][Q | dO] tiles, then [buffer][L | D] rows (64 floats each).
+  // [buffer][Q | dO] tiles, then [buffer][L | D] rows.
   __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];
-  __shared__ __attribute__((aligned(1024))) float stat_[2][2][kQTile];
+  __shared__ __attribute__((aligned(1024))) float stat_[2][2][kStat];
+  __shared__ __attribute__((aligned(1024))) uint16_t vt_[kVLds ? kKeysPerWg * D : 8];
   FA2_LDS uint16_t* const sT = (FA2_LDS uint16_t*)smem_;
   FA2_LDS float* const sS = (FA2_LDS float*)&stat_[0][0][0];
+  FA2_LDS uint16_t* const sV = (FA2_LDS uint16_t*)vt_;
 
   const int N = a.N;
   // Key tiles with a low index see the most query tiles under the causal mask:
@@ -193,22 +207,24 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
   const float* __restrict__ lh = a.lse + (int64_t)bh * N;
   const float* __restrict__ dh = a.delta + (int64_t)bh * N;
 
-  const int it0 = kCausal ? (kt * kKeysPerWg) / kQTile : 0;  // first query tile that sees these keys
-  const int it1 = (N + kQTile - 1) / kQTile;
+  const int it0 = kCausal ? (kt * kKeysPerWg) / QT : 0;  // first query tile that sees these keys
+  const int it1 = (N + QT - 1) / QT;
 
   auto load_tile = [&](int it, int buf) __attribute__((always_inline)) {
-    load_rows<D, kQTile>(qh, sT + (2 * buf + 0) * kTile, it * kQTile, N, wave, lane);
-    load_rows<D, kQTile>(gh, sT + (2 * buf + 1) * kTile, it * kQTile, N, wave, lane);
+    load_rows<D, QT>(qh, sT + (2 * buf + 0) * kTile, it * QT, N, wave, lane);
+    load_rows<D, QT>(gh, sT + (2 * buf + 1) * kTile, it * QT, N, wave, lane);
     if (wave == 0) {
-      const int r = min(it * kQTile + lane, N - 1);
-      dma4(lh + r, sS + (2 * buf + 0) * kQTile);
-      dma4(dh + r, sS + (2 * buf + 1) * kQTile);
+      const int r = min(it * QT + lane, N - 1);
+      dma4(lh + r, sS + (2 * buf + 0) * kStat);
+      dma4(dh + r, sS + (2 * buf + 1) * kStat);
     }
   };
+  // V of the workgroup's keys (d = 256), complete at the loop's first barrier.
+  if constexpr (kVLds) load_rows<D, kKeysPerWg>(a.v + head_off, sV, kt * kKeysPerWg, N, wave, lane);
   load_tile(it0, 0);
 
   // K and V of this lane's key (B operands of S = Q K^T and dP = dO V^T).
-  V8 kf[KS], vf[KS];
+  V8 kf[KS], vf[kVLds ? 1 : KS];
   {
     const int r = min(my_k, N - 1);
     const uint16_t* kp = a.k + head_off + (int64_t)r * D + 8 * hl;
@@ -216,7 +232,7 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(kp + 16 * ks));
-      vf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(vp + 16 * ks));
+      if constexpr (!kVLds) vf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(vp + 16 * ks));
     }
   }
 
@@ -239,22 +255,49 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
     if (it + 1 < it1) load_tile(it + 1, buf ^ 1);
     const FA2_LDS uint16_t* tq = sT + (2 * buf + 0) * kTile;
     const FA2_LDS uint16_t* tg_ = sT + (2 * buf + 1) * kTile;
-    const FA2_LDS float* tL = sS + (2 * buf + 0) * kQTile;
-    const FA2_LDS float* tD = sS + (2 * buf + 1) * kQTile;
+    const FA2_LDS float* tL = sS + (2 * buf + 0) * kStat;
+    const FA2_LDS float* tD = sS + (2 * buf + 1) * kStat;
 #pragma unroll
-    for (int sb = 0; sb < kQTile / 32; ++sb) {
-      const int q0 = it * kQTile + sb * 32;
+    for (int sb = 0; sb < QT / 32; ++sb) {
+      const int q0 = it * QT + sb * 32;
       if (q0 >= N) break;
       if (kCausal && q0 + 31 < kw0) continue;  // every query precedes every key of this wave
+      // LDS byte offsets of this lane's operand reads.  Row reads (row r of a
+      // tile, chunk 2 ks + hl): the swizzle depends on r % 16 only, and
+      // (2 ks + hl) ^ z = 2 ks ^ (hl ^ z), so chunk ks sits at
+      // r * 2D + ((32 ks) ^ hz16).  Transposed reads (rows r1, r1 + 8, 4 head
+      // dims from 32 db + ...): likewise 64 db ^ w16.  At d = 256 (16 k-steps,
+      // 8 head-dim blocks) the offsets are formed at each use from five lane
+      // values derived here, in the loop, from an opaque lane index: held
+      // across the loop, the 48 distinct offsets would be spilled.
+      const int ln = kVLds ? (int)opaque_vgpr((uint32_t)lane) : lane;
+      const int lcol = ln & 31, lhl = (ln >> 5) & 1, ltg = (ln >> 4) & 3, ltl = ln & 15;
+      const uint32_t hz16 = (uint32_t)((lhl ^ swz<D>(lcol)) << 4);
+      const int x0 = 2 * (ltg & 1) + ((ltl & 3) >> 1);
+      const int x1 = 4 * (ltg >> 1) + (ltl >> 2);
+      const uint32_t w1_16 = (uint32_t)((x0 ^ swz<D>(x1)) << 4), w2_16 = (uint32_t)((x0 ^ swz<D>(x1 + 8)) << 4);
+      const uint32_t t1 = (uint32_t)(x1 * D * 2 + 8 * (ltl & 1));
+      auto qoff = [&](int ks) __attribute__((always_inline)) {
+        if constexpr (kVLds) return (uint32_t)((sb * 32 + lcol) * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
+        else return tile_byte<D>(sb * 32 + col, 2 * ks + hl);
+      };
       // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t off = tile_byte<D>(sb * 32 + col, 2 * ks + hl);
+        const uint32_t off = qoff(ks);
         const V8 aq = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)((const FA2_LDS char*)tq + off));
         const V8 ag = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)((const FA2_LDS char*)tg_ + off));
         s = E::mfma(aq, kf[ks], s);
-        dp = E::mfma(ag, vf[ks], dp);
+        if constexpr (kVLds) {
+          const uint32_t vo = (uint32_t)((wave * 32 + lcol) * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
+          const V8 bv = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)((const FA2_LDS char*)sV + vo));
+          dp = E::mfma(ag, bv, dp);
+        } else {
+          dp = E::mfma(ag, vf[ks], dp);
+        }
+        // (d = 256: operands loaded just before their products, not all ahead.)
+        if constexpr (kVLds) __builtin_amdgcn_sched_barrier(0);
       }
       // Element e of the accumulators is query q0 + 8*(e/4) + 4*hl + e%4 of this
       // lane's key; its L and D sit at the same offset in the stat rows.
@@ -294,8 +337,15 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int dim = 32 * db + 16 * (tg & 1) + 4 * (tl & 3);
-          const uint32_t o1 = tile_byte<D>(r1, dim >> 3) + 8 * ((dim >> 2) & 1);
-          const uint32_t o2 = tile_byte<D>(r2, dim >> 3) + 8 * ((dim >> 2) & 1);
+          uint32_t o1, o2;
+          if constexpr (kVLds) {
+            const uint32_t rb = (uint32_t)((sb * 32 + 16 * c) * D * 2) + t1;
+            o1 = rb + ((uint32_t)(64 * db) ^ w1_16);
+            o2 = rb + (uint32_t)(8 * D * 2) + ((uint32_t)(64 * db) ^ w2_16);
+          } else {
+            o1 = tile_byte<D>(r1, dim >> 3) + 8 * ((dim >> 2) & 1);
+            o2 = tile_byte<D>(r2, dim >> 3) + 8 * ((dim >> 2) & 1);
+          }
           const u32x2 g1 = __builtin_bit_cast(
               u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tg_ + o1)));
           const u32x2 g2 = __builtin_bit_cast(
@@ -306,6 +356,7 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
               u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tq + o2)));
           dvt[db] = E::mfma(__builtin_bit_cast(V8, u32x4{g1[0], g1[1], g2[0], g2[1]}), bp, dvt[db]);
           dkt[db] = E::mfma(__builtin_bit_cast(V8, u32x4{q1[0], q1[1], q2[0], q2[1]}), bd, dkt[db]);
+          if constexpr (kVLds) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }

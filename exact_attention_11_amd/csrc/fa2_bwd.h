@@ -179,6 +179,9 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
   constexpr int QT = kVLds ? 32 : kQTile;  // query rows per streamed tile
   constexpr int kTile = QT * D;
   constexpr int kStat = 64;  // floats per L or D row of the stat buffers (one copy of 64 lanes)
+  // Operand offsets formed at each use from a few lane values (below) from
+  // d = 128 on, where holding all of them across the loop costs spills.
+  constexpr bool kXorAddr = D >= 128;
 
   // [buffer][Q | dO] tiles, then [buffer][L | D] rows.
   __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];
@@ -266,11 +269,11 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
       // tile, chunk 2 ks + hl): the swizzle depends on r % 16 only, and
       // (2 ks + hl) ^ z = 2 ks ^ (hl ^ z), so chunk ks sits at
       // r * 2D + ((32 ks) ^ hz16).  Transposed reads (rows r1, r1 + 8, 4 head
-      // dims from 32 db + ...): likewise 64 db ^ w16.  At d = 256 (16 k-steps,
-      // 8 head-dim blocks) the offsets are formed at each use from five lane
-      // values derived here, in the loop, from an opaque lane index: held
-      // across the loop, the 48 distinct offsets would be spilled.
-      const int ln = kVLds ? (int)opaque_vgpr((uint32_t)lane) : lane;
+      // dims from 32 db + ...): likewise 64 db ^ w16.  From d = 128 on the
+      // offsets are formed at each use from five lane values derived here, in
+      // the loop, from an opaque lane index: held across the loop, the distinct
+      // offsets (48 at d = 256) would be spilled.
+      const int ln = kXorAddr ? (int)opaque_vgpr((uint32_t)lane) : lane;
       const int lcol = ln & 31, lhl = (ln >> 5) & 1, ltg = (ln >> 4) & 3, ltl = ln & 15;
       const uint32_t hz16 = (uint32_t)((lhl ^ swz<D>(lcol)) << 4);
       const int x0 = 2 * (ltg & 1) + ((ltl & 3) >> 1);
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
       const uint32_t w1_16 = (uint32_t)((x0 ^ swz<D>(x1)) << 4), w2_16 = (uint32_t)((x0 ^ swz<D>(x1 + 8)) << 4);
       const uint32_t t1 = (uint32_t)(x1 * D * 2 + 8 * (ltl & 1));
       auto qoff = [&](int ks) __attribute__((always_inline)) {
-        if constexpr (kVLds) return (uint32_t)((sb * 32 + lcol) * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
+        if constexpr (kXorAddr) return (uint32_t)((sb * 32 + lcol) * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
         else return tile_byte<D>(sb * 32 + col, 2 * ks + hl);
       };
       // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
         for (int db = 0; db < DB; ++db) {
           const int dim = 32 * db + 16 * (tg & 1) + 4 * (tl & 3);
           uint32_t o1, o2;
-          if constexpr (kVLds) {
+          if constexpr (kXorAddr) {
             const uint32_t rb = (uint32_t)((sb * 32 + 16 * c) * D * 2) + t1;
             o1 = rb + ((uint32_t)(64 * db) ^ w1_16);
             o2 = rb + (uint32_t)(8 * D * 2) + ((uint32_t)(64 * db) ^ w2_16);

@@ -111,6 +111,7 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2
                                           int wave, int lane) {
   constexpr int CPR = D / 8;
   constexpr int kPer = R * CPR / (64 * kWaves);
+  constexpr int kStride = 64 * kWaves / CPR;  // rows between a wave's consecutive copies
   static_assert(kPer * 64 * kWaves == R * CPR, "tile copy split");
   const uint16_t* base = head + (int64_t)r0 * D;
   const int last = N - 1 - r0;  // rows past it re-read row N - 1
@@ -119,6 +120,19 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2
   // instead of being kept (or spilled) across the caller's loop.  (At d = 64
   // the kernels have registers to spare and keep them.)
   const int ln = D >= 128 ? (int)opaque_vgpr((uint32_t)lane) : lane;
+  if (D == 128 && last >= R - 1) {
+    // Whole tile at d = 128: copy t reads 16 * t rows further on and the
+    // swizzle repeats every 16 rows, so one lane offset serves every copy and
+    // the row step goes in the scalar base.  (Measured slower at d = 64 and
+    // 256, where the kernels keep the per-copy offsets below.)
+    static_assert(D != 128 || kStride == 16, "row step of the whole-tile copies");
+    const int s0 = wave * 64 + ln;
+    const int row = s0 / CPR;
+    const uint32_t off = (uint32_t)(row * D * 2 + (((s0 % CPR) ^ swz<D>(row)) << 4));
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) dma16_sbase(base + t * kStride * D, off, dst + (t * kWaves + wave) * 64 * 8);
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     const int s0 = (t * kWaves + wave) * 64;

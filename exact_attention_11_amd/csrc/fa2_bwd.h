@@ -407,7 +407,10 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
   typedef typename E::V8 V8;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int kTile = kKTile * D;
+  // Keys per streamed tile: 32 at d = 256, where halving the score and dP
+  // accumulators (and the LDS) takes dQ's spills from 104 to ~70 registers.
+  constexpr int KT = D == 256 ? 32 : kKTile;
+  constexpr int kTile = KT * D;
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];  // [buffer][K | V]
   FA2_LDS uint16_t* const sT = (FA2_LDS uint16_t*)smem_;
@@ -431,11 +434,11 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
   const uint16_t* __restrict__ vh = a.v + head_off;
 
   const int kv_end = kCausal ? min(N, (qt + 1) * kRowsPerWg) : N;
-  const int nt = (kv_end + kKTile - 1) / kKTile;
+  const int nt = (kv_end + KT - 1) / KT;
 
   auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
-    load_rows<D, kKTile>(kh, sT + (2 * buf + 0) * kTile, j * kKTile, N, wave, lane);
-    load_rows<D, kKTile>(vh, sT + (2 * buf + 1) * kTile, j * kKTile, N, wave, lane);
+    load_rows<D, KT>(kh, sT + (2 * buf + 0) * kTile, j * KT, N, wave, lane);
+    load_rows<D, KT>(vh, sT + (2 * buf + 1) * kTile, j * KT, N, wave, lane);
   };
   load_tile(0, 0);
 
@@ -466,15 +469,15 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
     const int buf = j & 1;
     wait_vm_lds_barrier<0>();
     if (j + 1 < nt) load_tile(j + 1, buf ^ 1);
-    const int kv0 = j * kKTile;
+    const int kv0 = j * KT;
     const bool active = !kCausal || kv0 <= q_row0 + 31;
     if (!active) continue;  // wave-uniform; the barriers stay in step
     const FA2_LDS uint16_t* tk = sT + (2 * buf + 0) * kTile;
     const FA2_LDS uint16_t* tv = sT + (2 * buf + 1) * kTile;
-    // S^T = K Q^T and dP^T = V dO^T for 64 keys x this wave's 32 queries.
-    f32x16 s[2], dp[2];
+    // S^T = K Q^T and dP^T = V dO^T for KT keys x this wave's 32 queries.
+    f32x16 s[KT / 32], dp[KT / 32];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KT / 32; ++kb) {
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
 #pragma unroll
@@ -487,11 +490,11 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
       }
     }
     // Element (kb, e) is key kv0 + 32*kb + 8*(e/4) + 4*hl + e%4 of query my_q.
-    const bool need_mask = (kv0 + kKTile > N) || (kCausal && kv0 + kKTile - 1 > q_row0);
+    const bool need_mask = (kv0 + KT > N) || (kCausal && kv0 + KT - 1 > q_row0);
     const int base = kv0 + 4 * hl;
-    uint32_t pd[2][8];
+    uint32_t pd[KT / 32][8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
         float ds2[2];
@@ -508,9 +511,9 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
         pd[kb][e >> 1] = E::pack2(ds2[0], ds2[1]);
       }
     }
-    // dQ^T += K^T dS^T over the four 16-key k-steps.
+    // dQ^T += K^T dS^T over the 16-key k-steps.
 #pragma unroll
-    for (int c = 0; c < kKTile / 16; ++c) {
+    for (int c = 0; c < KT / 16; ++c) {
       const V8 bd = __builtin_bit_cast(V8, u32x4{pd[c >> 1][4 * (c & 1) + 0], pd[c >> 1][4 * (c & 1) + 1],
                                                  pd[c >> 1][4 * (c & 1) + 2], pd[c >> 1][4 * (c & 1) + 3]});
       const int r1 = 16 * c + 4 * (tg >> 1) + (tl >> 2);

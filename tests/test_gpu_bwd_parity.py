@@ -87,9 +87,12 @@ def test_bwd_parity_ragged_sweep(dtype, d, causal, N):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
-def test_bwd_parity_medium(dtype, causal):
-    _parity(2, 3, 700, 128, dtype, causal, seed=4)
+def test_bwd_parity_medium(dtype, d, causal):
+    """700 rows: several key and query workgroups and streamed tiles per head,
+    ending in a ragged one."""
+    _parity(2, 3, 700, d, dtype, causal, seed=4)
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])

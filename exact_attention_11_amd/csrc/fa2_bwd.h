@@ -56,9 +56,9 @@ constexpr int kDeltaRows = 16;           // fa2_bwd_delta: rows per workgroup (1
 // Workgroups per CU each kernel is compiled for: two (two wavefronts per SIMD,
 // at most 256 registers each) up to d = 128, so that one workgroup's products
 // overlap the other's softmax gradient and memory waits; one at d = 256, where
-// the accumulators alone take 256 registers.  (fa2_bwd_dkdv at d = 128 then
-// spills a few of its K/V operand registers, and still runs faster than at one
-// workgroup per CU.)
+// the accumulators alone take 256 registers.  (At d = 128 fa2_bwd_dkdv then
+// needs 255 registers, and fits them only because its LDS operand offsets are
+// formed at each use; see the lane values in its loop.)
 template <int D> constexpr int kDkdvWgPerCu = D <= 128 ? 2 : 1;
 template <int D> constexpr int kDqWgPerCu = D <= 128 ? 2 : 1;
 

@@ -313,8 +313,6 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
         } else {
           dp = E::mfma(ag, vf[ks], dp);
         }
-        // (d = 256: operands loaded just before their products, not all ahead.)
-        if constexpr (kVLds) __builtin_amdgcn_sched_barrier(0);
       }
       // Element e of the accumulators is query q0 + 8*(e/4) + 4*hl + e%4 of this
       // lane's key; its L and D sit at the same offset in the stat rows.
@@ -373,7 +371,6 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
               u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tq + o2)));
           dvt[db] = E::mfma(__builtin_bit_cast(V8, u32x4{g1[0], g1[1], g2[0], g2[1]}), bp, dvt[db]);
           dkt[db] = E::mfma(__builtin_bit_cast(V8, u32x4{q1[0], q1[1], q2[0], q2[1]}), bd, dkt[db]);
-          if constexpr (kVLds) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }

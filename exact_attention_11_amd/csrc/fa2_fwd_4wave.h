@@ -249,7 +249,6 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
       for (int i = 0; i < kPipe; ++i) fr[i] = k_frag(i);
 #pragma unroll
       for (int f = 0; f < kNs; ++f) {
-        __builtin_amdgcn_sched_barrier(0);
         s[f & 1] = E::mfma(fr[f % kPipe], qf[f >> 1], s[f & 1]);
         if (f + kPipe < kNs) fr[f % kPipe] = k_frag(f + kPipe);
       }
@@ -342,7 +341,6 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
       for (int i = 0; i < kPipe; ++i) fr[i] = v_frag(i);
 #pragma unroll
       for (int f = 0; f < kNpv; ++f) {
-        __builtin_amdgcn_sched_barrier(0);
         const int c = f / DB;
         const u32x4 bw = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1], pk[c >> 1][4 * (c & 1) + 2],
                           pk[c >> 1][4 * (c & 1) + 3]};

@@ -9,9 +9,16 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 
 Metric: forward TFLOP/s with FLOP = 4*B*H*N^2*d, halved under a causal mask.
 ``roofline`` relates the kernel's average launch time (HIP events on the launch
-stream) to the dense fp16/bf16 MFMA peak of MI355X (2.5 PFLOP/s).
+stream) to the dense fp16/bf16 MFMA peak of MI355X (2.5 PFLOP/s at 2.4 GHz) and
+to that peak scaled to the engine clock measured over the timed steps
+(``clock_ghz``, ``frac_at_measured_clock``; fa2_clock_sample before and after).
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded, strided sample of the
 same workload's query rows on all host cores and scales it to TFLOP/s.
+
+The default forward run also times the other named workloads (``workloads``:
+each with its rate, roofline fractions, clock and a short oracle sample) and
+forward plus gradients on the two 2048-token workloads (``fwd_bwd``, next to
+the pages' A100 figures for those shapes); ``--headline-only`` skips them.
 """
 from __future__ import annotations
 
@@ -28,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+PEAK_CLOCK_GHZ = 2.4       # engine clock the published MFMA peak assumes (256 CUs x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth, published
 PEAK_FP8_MFMA_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
 # The fp8 forward runs half its products (Q K^T) at the fp8 peak and half (P V)
@@ -274,35 +282,74 @@ def cpu_baseline_decode(w, q, k, v, lens, target_s: float = 12.0):
     }
 
 
-def time_steps(step, stream, args):
-    """Warm up (fixed count, then until min_warmup_ms has passed), then time
-    args.steps calls with HIP events on ``stream``.  Returns (ms_per_step,
-    avg_launch_ms, min_launch_ms, wall_ms_per_step, extra_warmup_steps)."""
+class Timing:
+    """What time_steps measured: ms_per_step (first event to last over the
+    steps), avg/min/median launch ms (per-step event pairs), wall ms per step,
+    the extra warm-up steps, and the engine clock over the timed steps (per XCD
+    the average clock of its busiest CU; clock_ghz is their mean)."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def time_steps(step, stream, args, steps=None, min_warmup_ms=None):
+    """Warm up (args.warmup calls, then until min_warmup_ms has passed), then
+    time ``steps`` calls with HIP events on ``stream``.  A clock sample
+    (fa2_clock_sample) is enqueued on the same stream right before the first
+    timed call and right after the last, so the engine clock over the timed
+    steps comes out per XCD."""
+    import statistics
+
     import torch
 
+    import exact_attention_11_amd as fa
+
+    steps = args.steps if steps is None else steps
+    min_warmup_ms = args.min_warmup_ms if min_warmup_ms is None else min_warmup_ms
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     extra = 0
     t_w0 = time.perf_counter()
-    while (time.perf_counter() - t_w0) * 1e3 < args.min_warmup_ms:
+    while (time.perf_counter() - t_w0) * 1e3 < min_warmup_ms:
         for _ in range(5):
             step()
         extra += 5
         torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    clk = [torch.zeros(4 * fa.CLOCK_BLOCKS, dtype=torch.int64, device="cuda") for _ in range(2)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    for i in range(args.steps):
+    fa.clock_sample(clk[0], stream)
+    for i in range(steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
+    fa.clock_sample(clk[1], stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall0
     launch_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
     total_ms = starts[0].elapsed_time(ends[-1])
-    return total_ms / args.steps, sum(launch_ms) / len(launch_ms), min(launch_ms), wall_s * 1e3 / args.steps, extra
+    per_cu = fa.clock_ghz(clk[0].cpu().tolist(), clk[1].cpu().tolist())
+    per_xcd = fa.xcd_clocks(per_cu)
+    ghz = sum(per_xcd.values()) / len(per_xcd) if per_xcd else None
+    return Timing(ms_per_step=total_ms / steps, avg_ms=sum(launch_ms) / len(launch_ms), min_ms=min(launch_ms),
+                  median_ms=statistics.median(launch_ms), wall_ms=wall_s * 1e3 / steps, extra=extra, steps=steps,
+                  clock_ghz=ghz, clock_ghz_min=min(per_xcd.values()) if per_xcd else None,
+                  clock_ghz_max=max(per_xcd.values()) if per_xcd else None, clock_xcds=len(per_xcd),
+                  clock_cus=len(per_cu))
+
+
+def clock_fields(t: "Timing", achieved: float, peak: float, unit_peak_at: float = PEAK_CLOCK_GHZ) -> dict:
+    """The measured engine clock and the fraction of the peak scaled to it
+    (the published peak assumes unit_peak_at GHz)."""
+    if not t.clock_ghz:
+        return {"clock_ghz": None, "frac_at_measured_clock": None}
+    return {"clock_ghz": round(t.clock_ghz, 4),
+            "clock_ghz_xcd_range": [round(t.clock_ghz_min, 4), round(t.clock_ghz_max, 4)],
+            "peak_at_measured_clock": round(peak * t.clock_ghz / unit_peak_at, 1),
+            "frac_at_measured_clock": round(achieved / (peak * t.clock_ghz / unit_peak_at), 4)}
 
 
 def run_decode(args) -> int:
@@ -327,11 +374,12 @@ def run_decode(args) -> int:
                   workspace=ws)
 
     nbytes = decode_bytes(w, lens.tolist())
-    ms_per_step, avg_ms, min_ms, wall_ms, extra = time_steps(step, stream, args)
+    t = time_steps(step, stream, args)
+    ms_per_step, avg_ms, extra = t.ms_per_step, t.avg_ms, t.extra
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
-    log(f"{args.steps} steps: {ms_per_step:.4f} ms/step (events), launch avg {avg_ms:.4f} ms, min {min_ms:.4f} ms, "
-        f"wall {wall_ms:.4f} ms/step -> {value:.1f} GB/s")
+    log(f"{args.steps} steps: {ms_per_step:.4f} ms/step (events), launch avg {avg_ms:.4f} ms, min {t.min_ms:.4f} ms, "
+        f"wall {t.wall_ms:.4f} ms/step -> {value:.1f} GB/s, clock {t.clock_ghz} GHz")
     result = {
         "metric": "decode GB/s of compulsory HBM traffic (cache rows, Q, O, L), % of MI355X 8 TB/s",
         "value": round(value, 2),
@@ -352,7 +400,8 @@ def run_decode(args) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": recorded_traffic(w.name, f"fa2_decode_{w.name[len('decode_'):]}_kernel_stats.md",
-                                                 DECODE_KERNEL_SOURCES)},
+                                                 DECODE_KERNEL_SOURCES),
+                     "clock_ghz": round(t.clock_ghz, 4) if t.clock_ghz else None},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -383,6 +432,8 @@ def main() -> int:
                     help="time the forward pass (the headline), the gradient pass of the workload, or decode "
                          "against a key/value cache (a decode workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="forward pass: time only --workload, not the other workloads and fwd+bwd lines")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -495,11 +546,13 @@ def main() -> int:
     # time_steps keeps running untimed steps until the warm-up has lasted
     # min_warmup_ms so the timed steps see the steady clock (the count is
     # reported in the JSON line).
-    ms_per_step, avg_launch_ms, min_ms, wall_ms, extra = time_steps(step, stream, args)
+    t = time_steps(step, stream, args)
+    ms_per_step, avg_launch_ms, extra = t.ms_per_step, t.avg_ms, t.extra
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
     log(f"{args.steps} steps: {ms_per_step:.4f} ms/step (events), launch avg {avg_launch_ms:.4f} ms, "
-        f"min {min_ms:.4f} ms, wall {wall_ms:.4f} ms/step -> {value:.1f} TFLOP/s")
+        f"min {t.min_ms:.4f} ms, wall {t.wall_ms:.4f} ms/step -> {value:.1f} TFLOP/s; engine clock "
+        f"{t.clock_ghz} GHz over {t.clock_xcds} XCDs")
 
     traffic = recorded_traffic(w.name) if args.pass_ == "fwd" and not masked and not args.fp8 else None
     result = {
@@ -522,7 +575,7 @@ def main() -> int:
                        KERNEL_SOURCES if args.pass_ == "fwd" else BWD_KERNEL_SOURCES)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic},
+                     "traffic": traffic, **clock_fields(t, achieved, peak)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -536,8 +589,95 @@ def main() -> int:
         else:
             result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, dout_h, args.cpu_seconds)
         log(f"cpu baseline: {result['cpu_baseline']}")
+    if args.pass_ == "fwd" and not masked and not args.fp8 and not args.headline_only:
+        del q, k, v, dq, dk, dv, o, lse
+        torch.cuda.empty_cache()
+        result["workloads"] = [measure_forward(WORKLOADS[n], args)
+                               for n in WORKLOADS if n != w.name]
+        result["fwd_bwd"] = [measure_fwd_bwd(WORKLOADS[n], args) for n in FWD_BWD_WORKLOADS]
     print(json.dumps(result), flush=True)
     return 0
+
+
+# The pages' A100 fwd+bwd context ("FlashAttention-2: Where the Second 2x
+# Actually Comes From", Benchmarks): about 190 TFLOP/s at head dim 64, sequence
+# 2k, no mask, and about 160 at head dim 128, sequence 2k, causal (FP16, read
+# from plots).  The two 2048-token workloads have those shapes.
+FWD_BWD_WORKLOADS = {"b8h16_n2048_d64": 190.0, "b8h16_n2048_d128_causal": 160.0}
+
+
+def measure_forward(w, args) -> dict:
+    """One forward workload other than the headline: a few timed steps (the
+    tiny one: many, reported by the median launch), its rate against the MFMA
+    peak at 2.4 GHz and at the measured clock, and a short oracle sample on
+    the host cores."""
+    import torch
+
+    import exact_attention_11_amd as fa
+    from exact_attention_11_amd.inputs import workload_inputs
+
+    log(f"workload {w.name}: {w.what} (fwd pass)")
+    q, k, v = workload_inputs(w, seed=0)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.forward(dq, dk, dv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+
+    tiny = w.N * w.B * w.H <= 4096
+    t = time_steps(step, stream, args, steps=200 if tiny else max(args.steps, 20), min_warmup_ms=150.0)
+    flop = flop_count(w.B, w.H, w.N, w.d, w.causal)
+    ms = t.median_ms if tiny else t.ms_per_step
+    achieved = flop / ((t.median_ms if tiny else t.avg_ms) * 1e-3) / 1e12
+    value = flop / (ms * 1e-3) / 1e12
+    log(f"  {t.steps} steps: {t.ms_per_step:.4f} ms/step, launch avg {t.avg_ms:.4f} median {t.median_ms:.4f} ms "
+        f"-> {value:.1f} TFLOP/s, clock {t.clock_ghz} GHz")
+    out = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype, "causal": w.causal,
+           "inputs": w.dist, "flop_per_step": flop, "steps": t.steps,
+           "ms_per_step": round(ms, 5), "timing": "median launch" if tiny else "events over the steps",
+           "value": round(value, 3), "unit": "TFLOP/s",
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_MFMA_TFLOPS,
+                        "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), **clock_fields(t, achieved, PEAK_MFMA_TFLOPS)},
+           "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, min(args.cpu_seconds, 3.0))
+        log(f"  cpu baseline: {out['cpu_baseline']['value']:.4f} TFLOP/s on {out['cpu_baseline']['cores']} threads")
+    return out
+
+
+def measure_fwd_bwd(w, args) -> dict:
+    """Forward plus gradient pass of a workload per step, counted as 3.5x the
+    forward's FLOP (the forward's two products plus five in the gradients),
+    next to the pages' A100 figure for that shape."""
+    import torch
+
+    import exact_attention_11_amd as fa
+    from exact_attention_11_amd.inputs import workload_inputs
+
+    log(f"workload {w.name}: forward + gradients")
+    q, k, v = (t_.cuda() for t_ in workload_inputs(w, seed=0))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    dout = torch.randn((w.B, w.H, w.N, w.d), generator=torch.Generator().manual_seed(1)).to(q.dtype).cuda()
+    delta = torch.empty_like(lse)
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        fa.backward(q, k, v, o, dout, lse, causal=w.causal, scale=w.scale, stream=stream, delta=delta,
+                    dq=gq, dk=gk, dv=gv)
+
+    t = time_steps(step, stream, args, steps=max(args.steps, 20), min_warmup_ms=150.0)
+    flop = 3.5 * flop_count(w.B, w.H, w.N, w.d, w.causal)
+    value = flop / (t.ms_per_step * 1e-3) / 1e12
+    log(f"  {t.steps} steps: {t.ms_per_step:.4f} ms/step -> {value:.1f} TFLOP/s fwd+bwd, clock {t.clock_ghz} GHz")
+    return {"workload": w.name, "pass": "fwd+bwd", "flop_per_step": flop, "steps": t.steps,
+            "ms_per_step": round(t.ms_per_step, 5), "value": round(value, 3), "unit": "TFLOP/s",
+            "frac": round(value / PEAK_MFMA_TFLOPS, 4), "clock_ghz": round(t.clock_ghz, 4) if t.clock_ghz else None,
+            "pages_a100_context_tflops": FWD_BWD_WORKLOADS[w.name]}
 
 
 if __name__ == "__main__":

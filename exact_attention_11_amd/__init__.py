@@ -40,8 +40,9 @@ FA2_ERR_MASK = 10
 FA2_ERR_WORKSPACE = 11
 
 # Every symbol include/fa2.h declares.
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_fwd_fp8", "fa2_bwd", "fa2_decode", "fa2_decode_workspace_bytes",
-                    "fa2_status_str", "fa2_last_hip_error")
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_fwd_fp8", "fa2_bwd", "fa2_decode",
+                    "fa2_decode_workspace_bytes", "fa2_clock_sample", "fa2_status_str", "fa2_last_hip_error")
+CLOCK_BLOCKS = 2048  # FA2_CLOCK_BLOCKS
 DECODE_MAX_QUERIES = 8
 
 
@@ -94,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_decode.restype = ctypes.c_int
     lib.fa2_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
     lib.fa2_decode_workspace_bytes.restype = i64
+    lib.fa2_clock_sample.argtypes = [vp, vp]
+    lib.fa2_clock_sample.restype = ctypes.c_int
     lib.fa2_status_str.argtypes = [ctypes.c_int]
     lib.fa2_status_str.restype = ctypes.c_char_p
     lib.fa2_last_hip_error.argtypes = []
@@ -142,6 +145,58 @@ def fa2_decode(q: int, k: int, v: int, seqlens: int | None, o: int, lse: int, B:
 def fa2_decode_workspace_bytes(B: int, H: int, Mq: int, Nk: int, d: int) -> int:
     """Workspace bytes fa2_decode needs (0: none), or minus a status code."""
     return load_library().fa2_decode_workspace_bytes(B, H, Mq, Nk, d)
+
+
+def fa2_clock_sample(out: int, stream: int) -> int:
+    """Direct call of the clock-sample entry point (out: device address of
+    4 * CLOCK_BLOCKS uint64 values); returns the status."""
+    return load_library().fa2_clock_sample(out, stream)
+
+
+def clock_sample(out, stream=None):
+    """Enqueue fa2_clock_sample into ``out`` (an int64 device tensor of
+    4 * CLOCK_BLOCKS elements) on ``stream`` (default: the current stream)."""
+    import torch
+
+    if out.dtype != torch.int64 or out.numel() != 4 * CLOCK_BLOCKS or not out.is_cuda or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous int64 device tensor of {4 * CLOCK_BLOCKS} elements")
+    with torch.cuda.device(out.device):
+        s = stream if stream is not None else torch.cuda.current_stream(out.device)
+        rc = fa2_clock_sample(out.data_ptr(), s.cuda_stream)
+    if rc != FA2_OK:
+        raise Fa2Error(rc, fa2_status_str(rc), "fa2_clock_sample")
+    return out
+
+
+def clock_ghz(before, after):
+    """Average engine clock (GHz) between two clock samples (host sequences of
+    4 * CLOCK_BLOCKS integers from fa2_clock_sample), per CU: each CU's own
+    shader-clock counter difference over the real-time difference (100 MHz
+    ticks), from the first record of that CU in each sample.  Returns
+    {(xcd, cu key): GHz} for the CUs seen in both samples."""
+    def first(sample):
+        seen = {}
+        for i in range(len(sample) // 4):
+            xcc, hw, t, r = (int(x) for x in sample[4 * i:4 * i + 4])
+            seen.setdefault((xcc, (hw >> 8) & 0xFF), (t, r))
+        return seen
+
+    b, a = first(list(before)), first(list(after))
+    out = {}
+    for cu in sorted(set(b) & set(a)):
+        dt, dr = a[cu][0] - b[cu][0], a[cu][1] - b[cu][1]
+        if dr > 0 and dt > 0:
+            out[cu] = dt / dr * 0.1
+    return out
+
+
+def xcd_clocks(per_cu: dict) -> dict:
+    """Per XCD, the clock of its busiest CU (the largest per-CU average: a CU's
+    counter almost stops while it idles, so less busy CUs read low)."""
+    out = {}
+    for (xcc, _), ghz in per_cu.items():
+        out[xcc] = max(out.get(xcc, 0.0), ghz)
+    return out
 
 
 def fa2_status_str(status: int) -> str:
@@ -244,23 +299,63 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
         raise ValueError("lse must be float32 [B, H, N]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    own_delta = delta is None
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if own_delta else delta
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     for t in (dq, dk, dv):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
             raise ValueError("dq, dk, dv must be contiguous tensors like q")
-    if delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous():
-        raise ValueError("delta must be a contiguous float32 [B, H, N] tensor")
+    if (delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous()
+            or not delta.is_cuda or delta.device != q.device):
+        raise ValueError("delta must be a contiguous float32 [B, H, N] tensor on q's device")
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        if own_delta:
+            # delta is dropped on return while the kernels may still use it on s:
+            # the caching allocator must not hand its block to other streams first.
+            delta.record_stream(s)
         rc = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                      delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
                      int(bool(causal)), float(scale), code, s.cuda_stream)
     if rc != FA2_OK:
         raise Fa2Error(rc, fa2_status_str(rc), "fa2_bwd")
     return dq, dk, dv
+
+
+def _decode_args(q, k, v, seqlens, out, lse):
+    """Checks of decode(); returns (B, H, Mq, Nk, d,
+    dtype code, seqlens address, out, lse)."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"expected q [B, H, Mq, d] and k, v [B, H, Nk, d], got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    code = _dtype_code(q)
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, Mq, d = q.shape
+    Nk = k.shape[2]
+    len_ptr = None
+    if seqlens is not None:
+        if (seqlens.shape != (B,) or seqlens.dtype != torch.int32 or not seqlens.is_contiguous()
+                or seqlens.device != q.device):
+            raise ValueError("seqlens must be a contiguous int32 [B] tensor on q's device")
+        len_ptr = seqlens.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Mq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, Mq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, Mq] tensor on q's device")
+    return B, H, Mq, Nk, d, code, len_ptr, out, lse
 
 
 def decode(q, k, v, seqlens=None, causal: bool = False, scale: float | None = None, out=None, lse=None,
@@ -276,43 +371,26 @@ def decode(q, k, v, seqlens=None, causal: bool = False, scale: float | None = No
     """
     import torch
 
-    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
-        raise ValueError(f"expected q [B, H, Mq, d] and k, v [B, H, Nk, d], got {tuple(q.shape)}, "
-                         f"{tuple(k.shape)}, {tuple(v.shape)}")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k, v must share one dtype")
-    code = _dtype_code(q)
-    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
-        raise ValueError("q, k, v must be on one GPU")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
-    B, H, Mq, d = q.shape
-    Nk = k.shape[2]
+    B, H, Mq, Nk, d, code, len_ptr, out, lse = _decode_args(q, k, v, seqlens, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    len_ptr = None
-    if seqlens is not None:
-        if (seqlens.shape != (B,) or seqlens.dtype != torch.int32 or not seqlens.is_contiguous()
-                or seqlens.device != q.device):
-            raise ValueError("seqlens must be a contiguous int32 [B] tensor on q's device")
-        len_ptr = seqlens.data_ptr()
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Mq), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, Mq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
-        raise ValueError("lse must be a contiguous float32 [B, H, Mq] tensor on q's device")
     need = fa2_decode_workspace_bytes(B, H, Mq, Nk, d)
     if need < 0:
         raise Fa2Error(-need, fa2_status_str(-need), "fa2_decode")
-    if workspace is None and need > 0:
+    own_ws = workspace is None and need > 0
+    if own_ws:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace is not None and (not workspace.is_cuda or workspace.device != q.device
+                                    or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        if own_ws:
+            # The workspace is dropped on return while the kernels may still use
+            # it on s: keep its block from other streams until they are done.
+            workspace.record_stream(s)
         rc = fa2_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), len_ptr, out.data_ptr(), lse.data_ptr(),
                         B, H, Mq, Nk, d, int(bool(causal)), float(scale), code, ws_ptr, ws_bytes, s.cuda_stream)
     if rc != FA2_OK:

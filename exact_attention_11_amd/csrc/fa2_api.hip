@@ -55,6 +55,24 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
 // Query rows per workgroup of the kernel that serves head dim d.
 int64_t rows_per_workgroup(int64_t d) { return d == 256 ? fa2::w4::kBr : fa2::w8::kBr; }
 
+// One workgroup's sample for fa2_clock_sample: its XCD, its HW_ID (which CU),
+// that CU's shader-clock counter and the real-time counter.  Thread 0 writes
+// with vector stores.
+__global__ void fa2_clock_kernel(uint64_t* out) {
+  uint32_t xcc, hw;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+  const uint64_t t = __builtin_amdgcn_s_memtime();
+  const uint64_t r = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    uint64_t* o = out + 4 * blockIdx.x;
+    o[0] = xcc & 15u;
+    o[1] = hw;
+    o[2] = t;
+    o[3] = r;
+  }
+}
+
 template <int kDType, int D, int kMask>
 hipError_t launch(const fa2::FwdArgs& args, hipStream_t stream) {
   if constexpr (D == 256) {
@@ -212,6 +230,21 @@ const char* fa2_status_str(int status) {
 }
 
 int fa2_last_hip_error(void) { return g_last_hip_error; }
+
+int fa2_clock_sample(uint64_t* out, void* stream) {
+  g_last_hip_error = 0;
+  if (!out) return FA2_ERR_NULLPTR;
+  if (((uintptr_t)out) & 15) return FA2_ERR_ALIGN;
+  const int dev_status = check_device();
+  if (dev_status != FA2_OK) return dev_status;
+  hipLaunchKernelGGL(fa2_clock_kernel, dim3(FA2_CLOCK_BLOCKS), dim3(64), 0, (hipStream_t)stream, out);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA2_ERR_LAUNCH;
+  }
+  return FA2_OK;
+}
 
 int fa2_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                    int64_t N, int64_t d, const fa2_mask* mask, float scale, int dtype, void* stream) {

@@ -237,11 +237,37 @@ int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse
  * fa2_status code for sizes fa2_decode would reject.  Host only; no HIP call. */
 int64_t fa2_decode_workspace_bytes(int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d);
 
+/*
+ * fa2_clock_sample -- measurement aid, not part of the attention computation:
+ * enqueue on `stream` one small kernel of FA2_CLOCK_BLOCKS workgroups (enough
+ * for every CU of the chip to run some), each of which writes four uint64
+ * values to out[4*i .. 4*i+3] (i = its workgroup index): the id of the XCD it
+ * ran on, its HW_ID register (bits 8-15 name the CU, shader array and shader
+ * engine), that CU's shader-clock counter (s_memtime) and the 100 MHz
+ * real-time counter (s_memrealtime).  Each CU has its own shader-clock
+ * counter, which advances at the engine clock while the CU is busy and almost
+ * stops while it idles; so two samples taken around a run of launches on the
+ * same stream, matched CU by CU, give each CU's average engine clock over the
+ * run: (counter difference) / (real-time difference) x 100 MHz.  Utilisation
+ * is a ratio to a peak that assumes one clock ("6.2 FlashAttention V2 in
+ * depth", sections 1.1 and 8.1); the measured clock turns it into the ratio to
+ * the peak at the clock the chip actually ran.
+ *
+ * out    : device pointer to 4 * FA2_CLOCK_BLOCKS uint64 values, 16-byte
+ *          aligned; written.
+ * stream : as for fa2_fwd.
+ * Returns FA2_OK, FA2_ERR_NULLPTR, FA2_ERR_ALIGN, FA2_ERR_DEVICE or
+ * FA2_ERR_LAUNCH; checks run before any launch.
+ */
+#define FA2_CLOCK_BLOCKS 2048
+int fa2_clock_sample(uint64_t* out, void* stream);
+
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char* fa2_status_str(int status);
 
 /* Last HIP error code seen by a failing fa2_fwd, fa2_fwd_masked, fa2_fwd_fp8,
- * fa2_bwd or fa2_decode call on this thread (0 if none); useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
+ * fa2_bwd, fa2_decode or fa2_clock_sample call on this
+ * thread (0 if none); useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
 int fa2_last_hip_error(void);
 
 #ifdef __cplusplus

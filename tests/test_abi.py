@@ -317,3 +317,33 @@ def test_python_fp8_forward_rejects_bad_tensors(lib):
     with pytest.raises(TypeError):
         fa.forward_fp8(v, v, v)
 
+
+
+# --- fa2_clock_sample ----------------------------------------------------------------
+
+def test_clock_sample_argument_checks(lib):
+    assert fa.fa2_clock_sample(0, None) == fa.FA2_ERR_NULLPTR
+    assert fa.fa2_clock_sample(O + 8, None) == fa.FA2_ERR_ALIGN
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this call would launch on a fake pointer")
+    assert fa.fa2_clock_sample(O, None) == fa.FA2_ERR_DEVICE
+
+
+def test_clock_ghz_from_samples():
+    # two samples 1 ms apart in real time (100 000 ticks): on XCD 0 two CUs whose
+    # counters advanced 2.0e6 and 1.8e6 cycles (the second idled part of the
+    # time), on XCD 1 one CU that advanced 1.9e6: 2.0, 1.8 and 1.9 GHz per CU,
+    # 2.0 and 1.9 GHz per XCD
+    n = fa.CLOCK_BLOCKS
+    cus = [(0, 0x100, 2_000_000), (0, 0x200, 1_800_000), (1, 0x100, 1_900_000)]
+    before, after = [0] * (4 * n), [0] * (4 * n)
+    for i in range(n):
+        x, hw, adv = cus[i % 3]
+        before[4 * i:4 * i + 4] = [x, hw | (i & 0xff), 1000 * (hw >> 8) + x, 50]
+        after[4 * i:4 * i + 4] = [x, hw, 1000 * (hw >> 8) + x + adv, 100_050]
+    per_cu = fa.clock_ghz(before, after)
+    assert sorted(per_cu) == [(0, 1), (0, 2), (1, 1)]
+    assert abs(per_cu[(0, 1)] - 2.0) < 1e-12 and abs(per_cu[(0, 2)] - 1.8) < 1e-12
+    assert abs(per_cu[(1, 1)] - 1.9) < 1e-12
+    assert fa.xcd_clocks(per_cu) == {0: per_cu[(0, 1)], 1: per_cu[(1, 1)]}

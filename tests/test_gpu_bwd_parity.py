@@ -115,3 +115,40 @@ def test_bwd_deterministic_bitwise():
     b = _run(q, k, v, do, True, 0.1)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_bwd_rejects_host_delta_before_launch():
+    """A delta on the host (or another device) with device q, k, v is refused in
+    Python, before fa2_bwd could write through a host address."""
+    q, k, v = (t.cuda() for t in make_qkv(1, 2, 130, 64, torch.float16, "normal", 21))
+    o, lse = fa.forward(q, k, v, causal=True)
+    do = torch.randn_like(q)
+    with pytest.raises(ValueError):
+        fa.backward(q, k, v, o, do, lse, causal=True, delta=torch.empty(lse.shape, dtype=torch.float32))
+    torch.cuda.synchronize()
+
+
+def test_bwd_on_a_side_stream():
+    """Gradients launched on a stream other than the current one, with delta
+    allocated by backward() itself, equal the same call on the current stream
+    while the current stream keeps allocating (the dropped delta must not be
+    reused before the side stream's kernels finish)."""
+    q, k, v = make_qkv(2, 4, 1000, 128, torch.bfloat16, "normal", 22)
+    do = _dout(q.shape, torch.bfloat16, 22)
+    qc, kc, vc, gc = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.forward(qc, kc, vc, causal=True)
+    ref = fa.backward(qc, kc, vc, o, gc, lse, causal=True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        got = fa.backward(qc, kc, vc, o, gc, lse, causal=True, stream=s)
+        # work on the current stream that would reuse a freed delta block
+        junk = torch.full((2, 4, 1000), 7.0, device="cuda")
+        outs.append(got)
+        del junk
+    s.synchronize()
+    for got in outs:
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)

@@ -146,3 +146,25 @@ def test_decode_full_size_workload_sampled():
                                                        float(np.float32(w.scale)), seqlens=[int(lens[b])],
                                                        causal=w.causal)
             _check(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], o_ref, l_ref, w.torch_dtype, f"{name} b={b} h={h}")
+
+
+def test_decode_on_a_side_stream():
+    """Decode launched on a stream other than the current one with the workspace
+    allocated by decode() itself equals the same call on the current stream,
+    while the current stream keeps allocating and writing."""
+    B, H, Mq, Nk, d = 2, 4, 3, 6000, 128
+    q, k, v = make_decode_inputs(B, H, Mq, Nk, d, torch.float16, 23)
+    assert fa.fa2_decode_workspace_bytes(B, H, Mq, Nk, d) > 0
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    ref_o, ref_l = fa.decode(qc, kc, vc, causal=True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        outs.append(fa.decode(qc, kc, vc, causal=True, stream=s))
+        junk = torch.full((fa.fa2_decode_workspace_bytes(B, H, Mq, Nk, d) // 4,), 3.0, device="cuda")
+        del junk
+    s.synchronize()
+    for o, l in outs:
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l)

@@ -127,7 +127,7 @@ def test_parity_reference_moves(dtype, d, pattern):
 
     V is scaled by 1/4 (exact) so that |O| stays near 1, where the absolute
     tolerances apply: a single dominant weight can sit anywhere in (1, 2^8] and
-    keeps its rounding to the input type (2^-9 relative in bf16), so the error
+    keeps its rounding to the input type (2^-8 relative in bf16), so the error
     of O grows with |v| on such rows."""
     N = 320
     q, k, v = make_qkv(1, 1, N, d, dtype, "normal", 11)
@@ -156,6 +156,58 @@ def test_parity_reference_moves(dtype, d, pattern):
         o_ref, l_ref = oracle.attention_f64(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal,
                                             1.0)
         _compare(o, lse, o_ref, l_ref, dtype, f"{pattern} causal={causal}")
+
+
+@pytest.mark.parametrize("pattern", ["peaky", "overflow_jump", "plateau"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
+def test_lazy_reference_rounding_bound_unscaled_v(dtype, d, pattern):
+    """Values as large as they come (V ~ 4 N(0, 1), not scaled down), on rows
+    where a few keys carry most of the weight.  The weights are formed against a
+    reference max that may lag the row max by up to 2^8, rounded to the input
+    type (unit roundoff u = 2^-11 fp16, 2^-8 bf16) for P.V, and divided by a row
+    sum of the unrounded weights; O is rounded once at the end.  So every
+    element obeys |O - O_ref| <= u (A + |O_ref|) + 2 e A, where A = sum_c p_c |v_c|
+    is the oracle's output for |V| and e bounds the relative error of a weight
+    from fp32 arithmetic: the score sum in fp32 (at most (n - 1) 2^-24 |scale|
+    sum_t |q_t k_t| in the exponent for n nonzero products; none for the
+    constructed patterns, whose scores have one nonzero product), the fp32
+    multiplier scale * log2(e) and the fused multiply-add that applies it (2 u
+    |scale s| more), and a few fp32 ulps for the exponential.  The bound is relative: it holds at any |v|, where the
+    absolute tolerances of the other tests assume |O| near 1."""
+    N = 333
+    u = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}[dtype]
+    q, k, v = make_qkv(1, 2, N, d, dtype, "peaky", 31)
+    v = (torch.randn(v.shape, generator=torch.Generator().manual_seed(32)) * 4.0).to(dtype)
+    scale = 1.0 / math.sqrt(d)
+    if pattern != "peaky":
+        q = torch.zeros_like(q)
+        q[..., 0] = 1.0
+        k = torch.zeros_like(k)
+        sc = torch.zeros(N)
+        if pattern == "overflow_jump":
+            sc[100], sc[250] = 120.0, 240.0
+        else:
+            sc[64:192], sc[250:] = 5.0, 10.0
+        k[:, :, :, 0] = sc.to(dtype)
+        scale = 1.0
+    for causal in (False, True):
+        _log(f"case lazy reference bound {pattern} {dtype} d={d} causal={causal} max|v|={float(v.float().abs().max()):.2f}")
+        o, lse = _gpu_run(q, k, v, causal, scale)
+        qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+        o_ref, l_ref = oracle.attention_f64(qd, kd, vd, causal, _f32(scale))
+        a_ref, _ = oracle.attention_f64(qd, kd, np.abs(vd), causal, _f32(scale))
+        err = np.abs(o.double().numpy() - o_ref)
+        kt = kd.transpose(0, 1, 3, 2)
+        dots = np.abs(qd) @ np.abs(kt)                                   # sum_t |q_t k_t| per (row, key)
+        adds = np.maximum((qd != 0).astype(np.float64) @ (kt != 0).astype(np.float64) - 1.0, 0.0)
+        e_w = 2.0 ** -24 * abs(_f32(scale)) * ((adds + 2.0) * dots).max(axis=-1) + 2.0 ** -21
+        bound = u * (a_ref + np.abs(o_ref)) + 2.0 * e_w[..., None] * a_ref + 1e-6
+        ratio = float(np.max(err / bound))
+        _log(f"  max|dO|={float(err.max()):.3e} worst err/bound={ratio:.3f} max|dL|="
+             f"{float(np.max(np.abs(lse.double().numpy() - l_ref))):.3e}")
+        assert ratio <= 1.0, (ratio, np.unravel_index(np.argmax(err / bound), err.shape))
+        assert float(np.max(np.abs(lse.double().numpy() - l_ref))) <= TOL_L
 
 
 @pytest.mark.parametrize("B,H,N,d", [(1, 24, 4000, 64), (2, 8, 600, 128), (1, 16, 2500, 128)])
@@ -199,6 +251,32 @@ def test_parity_workload_full_size(name):
     # properties that hold at any size, over every row
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
     assert float(o.float().abs().max()) <= float(v.float().abs().max()) * (1 + 1e-2)
+    # every query tile of every (batch, head): two rows of each 128-row block (a
+    # workgroup covers one or two such blocks), one from each half, and the
+    # last row, so that every workgroup of the launch is compared
+    worst_o, worst_l, n_rows = 0.0, 0.0, 0
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = _rows_per_block(w.N, rng)
+            o_ref, l_ref = oracle.attention_rows_f64(q[b, h].double().numpy(), k[b, h].double().numpy(),
+                                                     v[b, h].double().numpy(), rows, w.causal, _f32(w.scale))
+            eo = float(np.max(np.abs(o[b, h, rows].double().numpy() - o_ref)))
+            el = float(np.max(np.abs(lse[b, h, rows].double().numpy() - l_ref)))
+            assert eo <= TOL_O[w.torch_dtype] and el <= TOL_L, ((b, h), eo, el)
+            worst_o, worst_l, n_rows = max(worst_o, eo), max(worst_l, el), n_rows + len(rows)
+    _log(f"  every query tile, {n_rows} rows over {w.B * w.H} heads: max|dO|={worst_o:.3e} max|dL|={worst_l:.3e}")
+
+
+def _rows_per_block(N, rng, block=128):
+    """Two rows of every block of ``block`` query rows (one in each half,
+    clipped to N) and the last row."""
+    rows = set()
+    for t in range(0, N, block):
+        half = block // 2
+        rows.add(min(N - 1, t + int(rng.integers(half))))
+        rows.add(min(N - 1, t + half + int(rng.integers(half))))
+    rows.add(N - 1)
+    return np.array(sorted(rows), dtype=np.int64)
 
 
 # --- the pages' worked examples, embedded at d = 64 ------------------------------------

@@ -38,10 +38,12 @@ FA2_ERR_DEVICE = 8
 FA2_ERR_LAUNCH = 9
 FA2_ERR_MASK = 10
 FA2_ERR_WORKSPACE = 11
+FA2_ERR_SCRATCH = 12
 
 # Every symbol include/fa2.h declares.
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_fwd_fp8", "fa2_bwd", "fa2_decode",
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_fwd_fp8", "fa2_bwd", "fa2_decode", "fa2_decode_static",
                     "fa2_decode_workspace_bytes", "fa2_clock_sample", "fa2_status_str", "fa2_last_hip_error")
+DECODE_STATIC_SCRATCH_BYTES = 4 << 20  # FA2_DECODE_STATIC_SCRATCH_BYTES
 CLOCK_BLOCKS = 2048  # FA2_CLOCK_BLOCKS
 DECODE_MAX_QUERIES = 8
 
@@ -93,6 +95,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                ctypes.c_int, vp, i64, vp]
     lib.fa2_decode.restype = ctypes.c_int
+    lib.fa2_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                      ctypes.c_int, vp]
+    lib.fa2_decode_static.restype = ctypes.c_int
     lib.fa2_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
     lib.fa2_decode_workspace_bytes.restype = i64
     lib.fa2_clock_sample.argtypes = [vp, vp]
@@ -140,6 +145,14 @@ def fa2_decode(q: int, k: int, v: int, seqlens: int | None, o: int, lse: int, B:
     """Direct call of the decode entry point with raw device addresses; returns the status."""
     return load_library().fa2_decode(q, k, v, seqlens, o, lse, B, H, Mq, Nk, d, int(causal), float(scale),
                                      int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def fa2_decode_static(q: int, k: int, v: int, seqlens: int | None, o: int, lse: int, B: int, H: int, Mq: int,
+                      Nk: int, d: int, causal: int, scale: float, dtype: int, stream: int) -> int:
+    """Direct call of the allocation-free decode entry point (chunk partials in
+    the library's fixed device scratch); returns the status."""
+    return load_library().fa2_decode_static(q, k, v, seqlens, o, lse, B, H, Mq, Nk, d, int(causal), float(scale),
+                                            int(dtype), stream)
 
 
 def fa2_decode_workspace_bytes(B: int, H: int, Mq: int, Nk: int, d: int) -> int:
@@ -325,7 +338,7 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
 
 
 def _decode_args(q, k, v, seqlens, out, lse):
-    """Checks of decode(); returns (B, H, Mq, Nk, d,
+    """Checks shared by decode() and decode_static(); returns (B, H, Mq, Nk, d,
     dtype code, seqlens address, out, lse)."""
     import torch
 
@@ -395,6 +408,26 @@ def decode(q, k, v, seqlens=None, causal: bool = False, scale: float | None = No
                         B, H, Mq, Nk, d, int(bool(causal)), float(scale), code, ws_ptr, ws_bytes, s.cuda_stream)
     if rc != FA2_OK:
         raise Fa2Error(rc, fa2_status_str(rc), "fa2_decode")
+    return out, lse
+
+
+def decode_static(q, k, v, seqlens=None, causal: bool = False, scale: float | None = None, out=None, lse=None,
+                  stream=None):
+    """decode() through fa2_decode_static: no workspace, the chunk partials go
+    to the library's fixed device scratch (at most DECODE_STATIC_SCRATCH_BYTES;
+    calls that may overlap on one device race on it).  With ``out`` and
+    ``lse`` given, this call allocates no device memory."""
+    import torch
+
+    B, H, Mq, Nk, d, code, len_ptr, out, lse = _decode_args(q, k, v, seqlens, out, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = fa2_decode_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), len_ptr, out.data_ptr(), lse.data_ptr(),
+                               B, H, Mq, Nk, d, int(bool(causal)), float(scale), code, s.cuda_stream)
+    if rc != FA2_OK:
+        raise Fa2Error(rc, fa2_status_str(rc), "fa2_decode_static")
     return out, lse
 
 

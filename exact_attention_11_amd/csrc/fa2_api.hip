@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "fa2.h"
 #include "fa2_bwd.h"
@@ -207,6 +208,115 @@ hipError_t launch_decode_d(const fa2::dec::DecArgs& args, int64_t d, hipStream_t
   }
 }
 
+// fa2_decode_static's scratch: the chunk partials of one call (normalised
+// outputs, then log2-sum-exps), at most kScratchBytes.  Each device holds its
+// own copy for the life of the process; calls on one device share it.  In host
+// code `scratch` names a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+constexpr int64_t kScratchBytes = FA2_DECODE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch_dev[kMaxDevices] = {nullptr};
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (looked up on first use), or an
+// error status.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    g_last_hip_error = (int)e;
+    (void)hipGetLastError();
+    return FA2_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_hip_error = (int)e;
+      (void)hipGetLastError();
+      return FA2_ERR_DEVICE;
+    }
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return FA2_OK;
+}
+
+// fa2_decode (caller's workspace) and fa2_decode_static (the device scratch
+// above): the same checks, plan and kernels.
+int decode_entry(const void* q, const void* k, const void* v, const int32_t* seqlens, void* o, float* lse,
+                 int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                 void* workspace, int64_t workspace_bytes, bool use_scratch, void* stream) {
+  g_last_hip_error = 0;
+  // ---- argument checks: no HIP call before they all pass -------------------
+  const int st = decode_shape_status(B, H, Mq, Nk, d);
+  if (st != FA2_OK) return st;
+  if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
+  const float c2 = (float)((double)scale * 1.4426950408889634074);
+  if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
+  const int64_t bh = B * H;
+  if (bh == 0 || Mq == 0) return FA2_OK;
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA2_ERR_NULLPTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA2_ERR_ALIGN;
+  if (((uintptr_t)seqlens) & 3) return FA2_ERR_ALIGN;
+  const int64_t need = decode_workspace(B, H, Mq, Nk, d);
+  if (use_scratch) {
+    if (need > kScratchBytes) return FA2_ERR_SCRATCH;
+  } else if (need > 0 && (!workspace || workspace_bytes < need || (((uintptr_t)workspace) & 15))) {
+    return FA2_ERR_WORKSPACE;
+  }
+  const uint64_t qb = (uint64_t)(bh * Mq * d) * 2, kb = (uint64_t)(bh * Nk * d) * 2;
+  const uint64_t lb = (uint64_t)(bh * Mq) * 4, sb = seqlens ? (uint64_t)B * 4 : 0;
+  const uint64_t wb = use_scratch ? 0 : (uint64_t)need;
+  const void* in[4] = {q, k, v, seqlens};
+  const uint64_t in_n[4] = {qb, kb, kb, sb};
+  const void* out[3] = {o, lse, workspace};
+  const uint64_t out_n[3] = {qb, lb, wb};
+  for (int i = 0; i < 3; ++i) {
+    if (out_n[i] == 0) continue;
+    for (int j = 0; j < 4; ++j)
+      if (in_n[j] > 0 && overlaps(out[i], out_n[i], in[j], in_n[j])) return FA2_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (out_n[j] > 0 && overlaps(out[i], out_n[i], out[j], out_n[j])) return FA2_ERR_ALIAS;
+  }
+
+  // ---- device ---------------------------------------------------------------
+  const int dev_status = check_device();
+  if (dev_status != FA2_OK) return dev_status;
+  if (use_scratch && need > 0) {
+    const int sc = scratch_address(&workspace);
+    if (sc != FA2_OK) return sc;
+  }
+
+  const DecodePlan plan = decode_plan(bh, Nk);
+  fa2::dec::DecArgs args;
+  args.q = (const uint16_t*)q;
+  args.k = (const uint16_t*)k;
+  args.v = (const uint16_t*)v;
+  args.o = (uint16_t*)o;
+  args.lse = lse;
+  args.seqlens = seqlens;
+  args.part_o = need > 0 ? (float*)workspace : nullptr;
+  args.part_lse = need > 0 ? (float*)workspace + plan.n_split * bh * Mq * d : nullptr;
+  args.H = (int)H;
+  args.Mq = (int)Mq;
+  args.Nk = (int)Nk;
+  args.n_split = (int)plan.n_split;
+  args.chunk = (int)plan.chunk;
+  args.causal = causal != 0;
+  args.n_bh = (int)bh;
+  args.c2 = c2;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_decode_d<0>(args, d, s) : launch_decode_d<1>(args, d, s);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA2_ERR_LAUNCH;
+  }
+  return FA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,6 +335,7 @@ const char* fa2_status_str(int status) {
     case FA2_ERR_LAUNCH: return "kernel launch failed";
     case FA2_ERR_MASK: return "mask: window bound below -1, negative prefix or misaligned segment ids";
     case FA2_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
+    case FA2_ERR_SCRATCH: return "problem needs more chunk scratch than fa2_decode_static holds (FA2_DECODE_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -418,64 +529,14 @@ int64_t fa2_decode_workspace_bytes(int64_t B, int64_t H, int64_t Mq, int64_t Nk,
 int fa2_decode(const void* q, const void* k, const void* v, const int32_t* seqlens, void* o, float* lse, int64_t B,
                int64_t H, int64_t Mq, int64_t Nk, int64_t d, int causal, float scale, int dtype, void* workspace,
                int64_t workspace_bytes, void* stream) {
-  g_last_hip_error = 0;
-  // ---- argument checks: no HIP call before they all pass -------------------
-  const int st = decode_shape_status(B, H, Mq, Nk, d);
-  if (st != FA2_OK) return st;
-  if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
-  const float c2 = (float)((double)scale * 1.4426950408889634074);
-  if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
-  const int64_t bh = B * H;
-  if (bh == 0 || Mq == 0) return FA2_OK;
-  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA2_ERR_NULLPTR;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA2_ERR_ALIGN;
-  if (((uintptr_t)seqlens) & 3) return FA2_ERR_ALIGN;
-  const int64_t need = decode_workspace(B, H, Mq, Nk, d);
-  if (need > 0 && (!workspace || workspace_bytes < need || (((uintptr_t)workspace) & 15))) return FA2_ERR_WORKSPACE;
-  const uint64_t qb = (uint64_t)(bh * Mq * d) * 2, kb = (uint64_t)(bh * Nk * d) * 2;
-  const uint64_t lb = (uint64_t)(bh * Mq) * 4, sb = seqlens ? (uint64_t)B * 4 : 0, wb = (uint64_t)need;
-  const void* in[4] = {q, k, v, seqlens};
-  const uint64_t in_n[4] = {qb, kb, kb, sb};
-  const void* out[3] = {o, lse, workspace};
-  const uint64_t out_n[3] = {qb, lb, wb};
-  for (int i = 0; i < 3; ++i) {
-    if (out_n[i] == 0) continue;
-    for (int j = 0; j < 4; ++j)
-      if (in_n[j] > 0 && overlaps(out[i], out_n[i], in[j], in_n[j])) return FA2_ERR_ALIAS;
-    for (int j = i + 1; j < 3; ++j)
-      if (out_n[j] > 0 && overlaps(out[i], out_n[i], out[j], out_n[j])) return FA2_ERR_ALIAS;
-  }
+  return decode_entry(q, k, v, seqlens, o, lse, B, H, Mq, Nk, d, causal, scale, dtype, workspace, workspace_bytes,
+                      false, stream);
+}
 
-  // ---- device ---------------------------------------------------------------
-  const int dev_status = check_device();
-  if (dev_status != FA2_OK) return dev_status;
-
-  const DecodePlan plan = decode_plan(bh, Nk);
-  fa2::dec::DecArgs args;
-  args.q = (const uint16_t*)q;
-  args.k = (const uint16_t*)k;
-  args.v = (const uint16_t*)v;
-  args.o = (uint16_t*)o;
-  args.lse = lse;
-  args.seqlens = seqlens;
-  args.part_o = need > 0 ? (float*)workspace : nullptr;
-  args.part_lse = need > 0 ? (float*)workspace + plan.n_split * bh * Mq * d : nullptr;
-  args.H = (int)H;
-  args.Mq = (int)Mq;
-  args.Nk = (int)Nk;
-  args.n_split = (int)plan.n_split;
-  args.chunk = (int)plan.chunk;
-  args.causal = causal != 0;
-  args.n_bh = (int)bh;
-  args.c2 = c2;
-
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_decode_d<0>(args, d, s) : launch_decode_d<1>(args, d, s);
-  if (e != hipSuccess) {
-    g_last_hip_error = (int)e;
-    return FA2_ERR_LAUNCH;
-  }
-  return FA2_OK;
+int fa2_decode_static(const void* q, const void* k, const void* v, const int32_t* seqlens, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                      void* stream) {
+  return decode_entry(q, k, v, seqlens, o, lse, B, H, Mq, Nk, d, causal, scale, dtype, nullptr, 0, true, stream);
 }
 
 int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,

@@ -53,8 +53,10 @@ typedef enum {
   FA2_ERR_LAUNCH = 9,  /* the HIP launch itself reported an error */
   FA2_ERR_MASK = 10,   /* fa2_fwd_masked: a window bound below -1, a negative
                           prefix, or segment ids not 4-byte aligned */
-  FA2_ERR_WORKSPACE = 11 /* fa2_decode: the workspace it needs is missing, smaller
+  FA2_ERR_WORKSPACE = 11, /* fa2_decode: the workspace it needs is missing, smaller
                             than fa2_decode_workspace_bytes, or not 16-byte aligned */
+  FA2_ERR_SCRATCH = 12    /* fa2_decode_static: the problem needs more than
+                             FA2_DECODE_STATIC_SCRATCH_BYTES of chunk scratch */
 } fa2_status;
 
 /*
@@ -207,6 +209,29 @@ int fa2_decode(const void* q, const void* k, const void* v, const int32_t* seqle
                void* stream);
 
 /*
+ * fa2_decode_static -- fa2_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation, arguments (minus the workspace), plan,
+ * kernels and results, with the chunk partials kept in a fixed device array of
+ * FA2_DECODE_STATIC_SCRATCH_BYTES that the library holds on every device it
+ * runs on until the process ends.  The call allocates nothing and calls no
+ * allocating routine; its first call on a device looks the array's address up
+ * (hipGetSymbolAddress) with that device current.
+ *
+ * Returns FA2_ERR_SCRATCH, before any HIP call, when fa2_decode_workspace_bytes
+ * for these sizes exceeds FA2_DECODE_STATIC_SCRATCH_BYTES; otherwise the
+ * statuses of fa2_decode (FA2_ERR_DEVICE also when the address lookup fails).
+ * Nothing in the array has to start at zero: every chunk writes its partial.
+ * All calls on one device share the array, so calls that can overlap on one
+ * device (on different streams, or from different threads) race and must be
+ * ordered by the caller; calls in order on one stream are safe.
+ */
+#define FA2_DECODE_STATIC_SCRATCH_BYTES (4 << 20)
+int fa2_decode_static(const void* q, const void* k, const void* v, const int32_t* seqlens,
+                      void* o, float* lse, int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d,
+                      int causal, float scale, int dtype, void* stream);
+
+/*
  * fa2_fwd_fp8 -- fa2_fwd with Q and K stored in fp8 (OCP e4m3, one byte per
  * element) and V, O in fp16 or bf16 (`dtype`): enqueue on `stream` and return
  * without waiting.  The real inputs are q_real = descale_q[b*H + h] * q and
@@ -266,7 +291,7 @@ int fa2_clock_sample(uint64_t* out, void* stream);
 const char* fa2_status_str(int status);
 
 /* Last HIP error code seen by a failing fa2_fwd, fa2_fwd_masked, fa2_fwd_fp8,
- * fa2_bwd, fa2_decode or fa2_clock_sample call on this
+ * fa2_bwd, fa2_decode, fa2_decode_static or fa2_clock_sample call on this
  * thread (0 if none); useful after FA2_ERR_DEVICE or FA2_ERR_LAUNCH. */
 int fa2_last_hip_error(void);
 

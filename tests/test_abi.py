@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 12):
+    for code in range(0, 13):
         s = fa.fa2_status_str(code)
         assert s and s != "unknown status"
     assert fa.fa2_status_str(123) == "unknown status"
@@ -317,6 +317,41 @@ def test_python_fp8_forward_rejects_bad_tensors(lib):
     with pytest.raises(TypeError):
         fa.forward_fp8(v, v, v)
 
+
+
+# --- fa2_decode_static ---------------------------------------------------------------
+
+def _dec_static(B=1, H=1, Mq=1, Nk=16, d=64, causal=0, scale=0.125, dtype=0, q=Q, k=K, v=V, seqlens=SL, o=O,
+                lse=L):
+    return fa.fa2_decode_static(q, k, v, seqlens, o, lse, B, H, Mq, Nk, d, causal, scale, dtype, None)
+
+
+def test_decode_static_scratch_limit(lib):
+    # the largest chunk partials the fixed scratch holds, and the first shapes past it
+    assert fa.fa2_decode_workspace_bytes(8, 32, 1, 16384, 128) <= fa.DECODE_STATIC_SCRATCH_BYTES
+    assert fa.fa2_decode_workspace_bytes(1, 64, 8, 16384, 256) > fa.DECODE_STATIC_SCRATCH_BYTES
+    assert _dec_static(B=1, H=64, Mq=8, Nk=16384, d=256) == fa.FA2_ERR_SCRATCH
+    assert _dec_static(B=2, H=100, Mq=8, Nk=16384, d=256) == fa.FA2_ERR_SCRATCH
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(B=-1), fa.FA2_ERR_SHAPE), (dict(Mq=9), fa.FA2_ERR_SHAPE), (dict(d=32), fa.FA2_ERR_HEADDIM),
+    (dict(dtype=2), fa.FA2_ERR_DTYPE), (dict(scale=math.inf), fa.FA2_ERR_SCALE), (dict(q=0), fa.FA2_ERR_NULLPTR),
+    (dict(o=O + 8), fa.FA2_ERR_ALIGN), (dict(seqlens=SL + 2), fa.FA2_ERR_ALIGN), (dict(o=Q), fa.FA2_ERR_ALIAS),
+    (dict(lse=SL), fa.FA2_ERR_ALIAS),
+])
+def test_decode_static_argument_checks(lib, kwargs, code):
+    assert _dec_static(**kwargs) == code
+
+
+def test_decode_static_empty_and_no_device(lib):
+    assert _dec_static(B=0) == fa.FA2_OK
+    assert _dec_static(Mq=0, q=0, o=0, lse=0) == fa.FA2_OK
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    assert _dec_static(Nk=5000, Mq=3, causal=1) == fa.FA2_ERR_DEVICE  # needs the scratch
+    assert _dec_static() == fa.FA2_ERR_DEVICE                        # one chunk: no scratch
 
 
 # --- fa2_clock_sample ----------------------------------------------------------------

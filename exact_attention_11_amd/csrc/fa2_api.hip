@@ -17,6 +17,7 @@
 #include "fa2_decode.h"
 #include "fa2_fwd_4wave.h"
 #include "fa2_fwd_8wave.h"
+#include "fa2_fwd_pair.h"
 
 namespace {
 
@@ -76,7 +77,11 @@ __global__ void fa2_clock_kernel(uint64_t* out) {
 
 template <int kDType, int D, int kMask>
 hipError_t launch(const fa2::FwdArgs& args, hipStream_t stream) {
-  if constexpr (D == 256) {
+  if constexpr (D == 256 && (kMask == fa2::kMaskNone || kMask == fa2::kMaskCausal)) {
+    static_assert(fa2::pr::kBr == fa2::w4::kBr, "both head-dim-256 kernels take the same query tiles");
+    hipLaunchKernelGGL((fa2::pr::fa2_fwd_pair<kDType, kMask>), dim3(args.n_wg), dim3(fa2::pr::kThreads), 0, stream,
+                       args);
+  } else if constexpr (D == 256) {
     hipLaunchKernelGGL((fa2::w4::fa2_fwd_4wave<kDType, D, kMask>), dim3(args.n_wg), dim3(fa2::w4::kThreads), 0,
                        stream, args);
   } else {

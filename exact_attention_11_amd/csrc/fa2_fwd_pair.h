@@ -399,26 +399,36 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   }
 
   // Epilogue: the row sum is the pair's two shares; one division per row, the
-  // logsumexp in natural-log units.
+  // logsumexp in natural-log units.  A lane holds 4-element pieces of one row,
+  // so this wavefront's half of O goes through LDS (free after the barriers
+  // below): written row-major, read back 16 bytes per lane and stored as whole
+  // 256-byte row halves, 1 KB per store instruction.
   const float l_mine = sum_pair32(l_part);
-  lds_done_barrier();  // every wavefront is done with sM
+  lds_done_barrier();  // every wavefront is done with the tiles and with sM
   sM[wave * 64 + lane] = l_mine;
   lds_done_barrier();
   const float l_row = l_mine + sM[partner * 64 + lane];
   const float inv = 1.f / l_row;
-  if (my_q < N) {
-    uint16_t* op = a.o + head_off + (int64_t)my_q * D + 128 * kh;
+  if (my_q < N && hl == 0 && kh == 0) a.lse[(int64_t)bh * N + my_q] = (m_run + __log2f(l_row)) * kLn2;
+  constexpr int kRowB = 256 + 16;  // staging row stride (bytes): rows start in different banks
+  static_assert(4 * 32 * kRowB <= 2 * kTile * 2, "a group's staging fits in its tile buffers");
+  FA2_LDS char* const stg = (FA2_LDS char*)(grp == 0 ? sK_ : sV_) + (wave & 3) * 32 * kRowB;
 #pragma unroll
-    for (int j = 0; j < DBH; ++j) {
+  for (int j = 0; j < DBH; ++j) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dim = 32 * j + 8 * r4 + 4 * hl;
-        const u32x2 wv = {E::pack2(o[j][4 * r4 + 0] * inv, o[j][4 * r4 + 1] * inv),
-                          E::pack2(o[j][4 * r4 + 2] * inv, o[j][4 * r4 + 3] * inv)};
-        *(u32x2*)(op + dim) = wv;
-      }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dim = 32 * j + 8 * r4 + 4 * hl;
+      const u32x2 wv = {E::pack2(o[j][4 * r4 + 0] * inv, o[j][4 * r4 + 1] * inv),
+                        E::pack2(o[j][4 * r4 + 2] * inv, o[j][4 * r4 + 3] * inv)};
+      *(FA2_LDS u32x2*)(stg + col * kRowB + dim * 2) = wv;
     }
-    if (hl == 0 && kh == 0) a.lse[(int64_t)bh * N + my_q] = (m_run + __log2f(l_row)) * kLn2;
+  }
+  const int sr = lane >> 4, sc = lane & 15;  // 16 lanes per 256-byte row half, 4 rows per store
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 4 * i + sr;
+    const u32x4 v = *(const FA2_LDS u32x4*)(stg + row * kRowB + sc * 16);
+    if (q_row0 + row < N) *(u32x4*)(a.o + head_off + (int64_t)(q_row0 + row) * D + 128 * kh + sc * 8) = v;
   }
 }
 

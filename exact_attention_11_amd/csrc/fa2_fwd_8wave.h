@@ -642,7 +642,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   const float l_row = sum_pair32(l_part);
   const float inv = 1.f / l_row;
   if (my_q < N && hl == 0) a.lse[(int64_t)bh * N + my_q] = (m_run + __log2f(l_row)) * kLn2;
-  constexpr int kRowB = D * 2 + 16;  // staging row stride (bytes), 16 more than a row: rows start in different banks
+  // Staging row stride: 16 bytes more than a row, which keeps the 16-byte reads
+  // aligned and conflict-free; the 8-byte writes of a half wave meet 2-way
+  // (about 0.05 % of the kernel's time on the long-context workload).
+  constexpr int kRowB = D * 2 + 16;
   static_assert(kWaves * 32 * kRowB <= (int)sizeof(smem_), "O staging fits in the tile buffers");
   lds_done_barrier();  // every wave is done with the tile buffers
   FA2_LDS char* const stg = (FA2_LDS char*)smem_ + wave * 32 * kRowB;

@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   const float l_row = l_mine + sM[partner * 64 + lane];
   const float inv = 1.f / l_row;
   if (my_q < N && hl == 0 && kh == 0) a.lse[(int64_t)bh * N + my_q] = (m_run + __log2f(l_row)) * kLn2;
-  constexpr int kRowB = 256 + 16;  // staging row stride (bytes): rows start in different banks
+  constexpr int kRowB = 256 + 16;  // staging row stride: aligned, conflict-free 16-byte reads
   static_assert(4 * 32 * kRowB <= 2 * kTile * 2, "a group's staging fits in its tile buffers");
   FA2_LDS char* const stg = (FA2_LDS char*)(grp == 0 ? sK_ : sV_) + (wave & 3) * 32 * kRowB;
 #pragma unroll

@@ -47,7 +47,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # The sources that define the kernels of each pass (a recorded profile applies
 # while their digest is unchanged).
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
-                  for f in ("fa2_common.h", "fa2_fwd_4wave.h", "fa2_fwd_8wave.h")]
+                  for f in ("fa2_common.h", "fa2_fwd_4wave.h", "fa2_fwd_8wave.h", "fa2_fwd_pair.h")]
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
                       for f in ("fa2_common.h", "fa2_bwd.h")]
 DECODE_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
@@ -639,7 +639,8 @@ def measure_forward(w, args) -> dict:
            "ms_per_step": round(ms, 5), "timing": "median launch" if tiny else "events over the steps",
            "value": round(value, 3), "unit": "TFLOP/s",
            "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_MFMA_TFLOPS,
-                        "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), **clock_fields(t, achieved, PEAK_MFMA_TFLOPS)},
+                        "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "traffic": recorded_traffic(w.name),
+                        **clock_fields(t, achieved, PEAK_MFMA_TFLOPS)},
            "cpu_baseline": None}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, min(args.cpu_seconds, 3.0))

@@ -86,11 +86,21 @@ def visible_pairs(N: int, causal: bool, window=None, prefix: int = 0, doc_len: i
     return float(np.sum(size(lo, hi) + size(pl, ph) - both))
 
 
+_TOKEN = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed: what a
+    compiler sees, so that editing a comment does not void a recorded profile."""
+    text = _TOKEN.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", src)
+    return " ".join(text.split())
+
+
 def kernel_source_digest(sources=None) -> str:
     h = hashlib.sha256()
     for p in sources or KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

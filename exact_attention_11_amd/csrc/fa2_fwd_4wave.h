@@ -190,9 +190,11 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   float l_part = 0.f;     // this lane's share of the row sum
 
   // Operand reads run as pipelines kPipe fragments ahead of the MFMAs that use
-  // them; the scheduling fences keep the compiler from hoisting every read of a
-  // phase (a register quad each), which would spill.  Consecutive MFMAs use
-  // different accumulators.
+  // them.  The reads of a loop cannot move above it (the wait-and-barrier
+  // before it clobbers memory); a scheduling fence after each loop keeps them
+  // from sinking into the code that follows, where the compiler would hold
+  // every read of a phase at once (a register quad each) and spill.
+  // Consecutive MFMAs use different accumulators.
   constexpr int kPipe = 4;
   V8 fr[kPipe];
   // S^T = K Q^T, fragment f: key block kb = f % 2, k-step ks = f / 2; lane

@@ -382,3 +382,22 @@ def test_clock_ghz_from_samples():
     assert abs(per_cu[(0, 1)] - 2.0) < 1e-12 and abs(per_cu[(0, 2)] - 1.8) < 1e-12
     assert abs(per_cu[(1, 1)] - 1.9) < 1e-12
     assert fa.xcd_clocks(per_cu) == {0: per_cu[(0, 1)], 1: per_cu[(1, 1)]}
+
+
+def test_profile_digest_ignores_comments_only():
+    # The digest that ties a recorded profile to the kernel sources changes with
+    # the code and not with its comments; string literals (inline assembly) are
+    # code, even when they hold comment markers.
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "bench_mod", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    a = 'int f(int x) {  // scale\n  return 2 * x; /* twice\n */ }\nconst char* s = "a // b";\n'
+    b = 'int f(int x) {\n  // new note\n  return 2 * x; }\nconst char* s = "a // b";  /* kept */\n'
+    c = 'int f(int x) { return 3 * x; }\nconst char* s = "a // b";\n'
+    d = 'int f(int x) { return 2 * x; }\nconst char* s = "a /* b";\n'
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert bench.code_text(a) != bench.code_text(d)
+    assert '"a // b"' in bench.code_text(a)

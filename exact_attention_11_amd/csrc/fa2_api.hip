@@ -18,6 +18,7 @@
 #include "fa2_fwd_4wave.h"
 #include "fa2_fwd_8wave.h"
 #include "fa2_fwd_pair.h"
+#include "fa2_fwd_w64.h"
 
 namespace {
 
@@ -84,6 +85,11 @@ hipError_t launch(const fa2::FwdArgs& args, hipStream_t stream) {
   } else if constexpr (D == 256) {
     hipLaunchKernelGGL((fa2::w4::fa2_fwd_4wave<kDType, D, kMask>), dim3(args.n_wg), dim3(fa2::w4::kThreads), 0,
                        stream, args);
+  } else if constexpr (D == 128 && (kDType == fa2::kFp16 || kDType == fa2::kBf16) &&
+                       (kMask == fa2::kMaskNone || kMask == fa2::kMaskCausal)) {
+    static_assert(fa2::w64::kBr == fa2::w8::kBr, "both head-dim-128 kernels take the same query tiles");
+    hipLaunchKernelGGL((fa2::w64::fa2_fwd_w64<kDType, kMask>), dim3(args.n_wg), dim3(fa2::w64::kThreads), 0, stream,
+                       args);
   } else {
     hipLaunchKernelGGL((fa2::w8::fa2_fwd_8wave<kDType, D, kMask>), dim3(args.n_wg), dim3(fa2::w8::kThreads), 0,
                        stream, args);

@@ -19,6 +19,9 @@ Contents
     The gradients dQ, dK, dV of that definition for a given dO (and the row
     statistic D), by the chain rule in fp64, implemented in
     ``attention_bwd_ref.c``.
+``attention_bwd_masked_f64``
+    The same gradients under a general mask (the mask of
+    ``attention_masked_f64``), implemented in ``attention_bwd_mask_ref.c``.
 ``attention_decode_f64``
     A few new query rows against a key/value cache with per-batch valid
     lengths (the last Mq positions of each sequence; causal or not),
@@ -45,17 +48,18 @@ _SRC = os.path.join(_HERE, "attention_ref.c")
 _BWD_SRC = os.path.join(_HERE, "attention_bwd_ref.c")
 _MASK_SRC = os.path.join(_HERE, "attention_mask_ref.c")
 _DECODE_SRC = os.path.join(_HERE, "attention_decode_ref.c")
+_BWD_MASK_SRC = os.path.join(_HERE, "attention_bwd_mask_ref.c")
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 _lib_cache: dict[str, ctypes.CDLL] = {}
 
 
 def build(src: str = _SRC, out: str = LIB_PATH, bwd_src: str = _BWD_SRC, mask_src: str = _MASK_SRC,
-          decode_src: str = _DECODE_SRC) -> str:
-    """Compile the C oracle (forward, gradient, general-mask and decode sources)
-    with gcc (no fast-math: IEEE fp64 throughout)."""
+          decode_src: str = _DECODE_SRC, bwd_mask_src: str = _BWD_MASK_SRC) -> str:
+    """Compile the C oracle (forward, gradient, general-mask, decode and
+    masked-gradient sources) with gcc (no fast-math: IEEE fp64 throughout)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-           "-ffp-contract=off", "-pthread", src, bwd_src, mask_src, decode_src, "-o", out, "-lm"]
+           "-ffp-contract=off", "-pthread", src, bwd_src, mask_src, decode_src, bwd_mask_src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -88,6 +92,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oracle_attention_decode_f64.argtypes = [dp, dp, dp, ip, dp, dp, i64, i64, i64, i64, i64,
                                                 ctypes.c_int, ctypes.c_double, ctypes.c_int]
     lib.oracle_attention_decode_f64.restype = ctypes.c_int
+    lib.oracle_attention_bwd_masked_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64,
+                                                    i64, ip, ctypes.c_double, ctypes.c_int]
+    lib.oracle_attention_bwd_masked_f64.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
 
@@ -230,6 +237,37 @@ def attention_masked_f64(q, k, v, scale: float, window_left: int = -1, window_ri
     if rc != 0:
         raise RuntimeError(f"oracle_attention_masked_f64 failed with code {rc}")
     return o, lse
+
+
+def attention_bwd_masked_f64(q, k, v, dout, scale: float, window_left: int = -1, window_right: int = -1,
+                             prefix: int = 0, segment_ids=None, causal: bool = False,
+                             nthreads: int | None = None, lib_path: str = LIB_PATH):
+    """Gradients of exact attention over [B, H, N, d] fp64 arrays under the
+    general mask of ``attention_masked_f64`` (same arguments).  Returns
+    ``(dq, dk, dv, delta)`` as ``attention_bwd_f64`` does.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    if not (q.shape == k.shape == v.shape == dout.shape) or q.ndim != 4:
+        raise ValueError("expected four [B, H, N, d] arrays of equal shape")
+    B, H, N, d = q.shape
+    wr = int(window_right)
+    if causal:
+        wr = 0 if wr < 0 else min(wr, 0)
+    seg_ptr = None
+    if segment_ids is not None:
+        seg = np.ascontiguousarray(np.asarray(segment_ids, dtype=np.int32))
+        if seg.shape != (B, N):
+            raise ValueError("segment_ids must be [B, N]")
+        seg_ptr = seg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    delta = np.empty((B, H, N), dtype=np.float64)
+    lib = load(lib_path)
+    rc = lib.oracle_attention_bwd_masked_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                             _ptr(delta), B, H, N, d, int(window_left), wr, int(prefix), seg_ptr,
+                                             float(scale), _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_bwd_masked_f64 failed with code {rc}")
+    return dq, dk, dv, delta
 
 
 def attention_decode_f64(q, k, v, scale: float, seqlens=None, causal: bool = False,

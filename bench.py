@@ -222,10 +222,12 @@ def decode_bytes(w, lens) -> float:
     return kv + qo + w.B * w.H * w.Mq * 4
 
 
-def cpu_baseline_masked(w, q, k, v, window, prefix, seg, pairs_per_head, target_s: float = 12.0):
-    """Time the fp64 general-mask oracle on whole heads of the workload, one head
-    per host thread per call, until about ``target_s`` seconds have passed; the
-    rate counts 4 d FLOP per visible (query, key) pair, like the GPU line."""
+def cpu_baseline_masked(w, q, k, v, window, prefix, seg, pairs_per_head, target_s: float = 12.0, dout=None):
+    """Time the fp64 general-mask oracle (with ``dout``: the masked gradient
+    oracle) on whole heads of the workload, one head per host thread per call,
+    until about ``target_s`` seconds have passed; the rate counts 4 d FLOP per
+    visible (query, key) pair for the forward and 2.5 times that for the
+    gradients, like the GPU line."""
     import numpy as np
 
     import oracle
@@ -243,18 +245,24 @@ def cpu_baseline_masked(w, q, k, v, window, prefix, seg, pairs_per_head, target_
         vs = np.stack([v[b, h].double().numpy() for b, h in batch])[:, None]
         segs = None if seg is None else np.stack([seg[b] for b, _ in batch])
         t0 = time.perf_counter()
-        oracle.attention_masked_f64(qs, ks, vs, scale, window_left=wl, window_right=wr, prefix=prefix,
-                                    segment_ids=segs, causal=w.causal, nthreads=threads)
+        if dout is None:
+            oracle.attention_masked_f64(qs, ks, vs, scale, window_left=wl, window_right=wr, prefix=prefix,
+                                        segment_ids=segs, causal=w.causal, nthreads=threads)
+        else:
+            gs = np.stack([dout[b, h].double().numpy() for b, h in batch])[:, None]
+            oracle.attention_bwd_masked_f64(qs, ks, vs, gs, scale, window_left=wl, window_right=wr, prefix=prefix,
+                                            segment_ids=segs, causal=w.causal, nthreads=threads)
         secs += time.perf_counter() - t0
-        flop += 4.0 * w.d * pairs_per_head * len(batch)
+        flop += (4.0 if dout is None else 10.0) * w.d * pairs_per_head * len(batch)
         done += len(batch)
+    kind = "general-mask oracle" if dout is None else "masked gradient oracle"
     return {
         "value": flop / secs / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"{done} whole head(s) of {w.name} under the mask: {flop / 1e9:.1f} GFLOP of visible pairs in "
-                  f"{secs:.1f} s (fp64 general-mask oracle)",
+                  f"{secs:.1f} s (fp64 {kind})",
     }
 
 
@@ -431,10 +439,10 @@ def main() -> int:
                     help="extra untimed steps until the warm-up has lasted this long (clock ramp-up)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--window", type=int, nargs=2, default=None, metavar=("LEFT", "RIGHT"),
-                    help="forward pass under a sliding window (-1: no bound on that side)")
-    ap.add_argument("--prefix", type=int, default=0, help="forward pass: keys below this are visible to every query")
+                    help="forward or gradient pass under a sliding window (-1: no bound on that side)")
+    ap.add_argument("--prefix", type=int, default=0, help="forward or gradient pass: keys below this are visible to every query")
     ap.add_argument("--documents", type=int, default=0,
-                    help="forward pass: split each sequence into this many equal contiguous documents")
+                    help="forward or gradient pass: split each sequence into this many equal contiguous documents")
     ap.add_argument("--fp8", action="store_true",
                     help="forward pass with Q and K in fp8 (e4m3, per-head scales) and V, O in the workload's "
                          "16-bit type (head dim 128)")
@@ -470,8 +478,11 @@ def main() -> int:
         log(f"copied {n} bytes 5 times")
         return 0
 
-    if args.pass_ != "fwd" and (args.window is not None or args.prefix > 0 or args.documents > 0 or args.fp8):
-        log("masks other than causal, and fp8 inputs, apply to the forward pass only")
+    if args.pass_ == "decode" and (args.window is not None or args.prefix > 0 or args.documents > 0):
+        log("masks other than causal apply to the forward and gradient passes only")
+        return 2
+    if args.pass_ != "fwd" and args.fp8:
+        log("fp8 inputs apply to the forward pass only")
         return 2
     if args.fp8 and (args.window is not None or args.prefix > 0 or args.documents > 0):
         log("the fp8 forward pass takes no mask or the causal mask")
@@ -493,6 +504,21 @@ def main() -> int:
     masked = args.window is not None or args.prefix > 0 or args.documents > 0
     mask_cfg = None
     peak = PEAK_MFMA_TFLOPS
+    if masked:
+        # contiguous documents of equal length; the same ids for every batch
+        doc_len = -(-w.N // args.documents) if args.documents > 0 else 0
+        seg = None
+        seg_host = None
+        if doc_len:
+            seg_host = (torch.arange(w.N, dtype=torch.int32) // doc_len).repeat(w.B, 1).contiguous()
+            seg = seg_host.cuda()
+        window = tuple(args.window) if args.window is not None else None
+        pairs = visible_pairs(w.N, w.causal, window, args.prefix, doc_len)
+        mask_cfg = {"window": list(window) if window else None, "prefix": args.prefix, "documents": args.documents,
+                    "visible_pairs_per_head": pairs}
+        mask_kw = dict(window=window, prefix=args.prefix, segment_ids=seg)
+    else:
+        mask_kw = {}
     if args.fp8:
         if w.d != 128:
             log("the fp8 forward pass serves head dim 128")
@@ -513,21 +539,9 @@ def main() -> int:
         k = k8.to(torch.float64) * dsk.to(torch.float64).reshape(w.B, w.H, 1, 1)
         v = v16
     elif args.pass_ == "fwd" and masked:
-        doc_len = -(-w.N // args.documents) if args.documents > 0 else 0
-        seg = None
-        seg_host = None
-        if doc_len:
-            seg_host = (torch.arange(w.N, dtype=torch.int32) // doc_len).repeat(w.B, 1).contiguous()
-            seg = seg_host.cuda()
-        window = tuple(args.window) if args.window is not None else None
-
         def step():
-            fa.forward(dq, dk, dv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream, window=window,
-                       prefix=args.prefix, segment_ids=seg)
-        pairs = visible_pairs(w.N, w.causal, window, args.prefix, doc_len)
+            fa.forward(dq, dk, dv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream, **mask_kw)
         flop = 4.0 * w.B * w.H * w.d * pairs
-        mask_cfg = {"window": list(window) if window else None, "prefix": args.prefix, "documents": args.documents,
-                    "visible_pairs_per_head": pairs}
         metric = "attention fwd TFLOP/s over visible pairs (general mask), % of MI355X FP16/BF16 MFMA peak"
     elif args.pass_ == "fwd":
         def step():
@@ -537,7 +551,7 @@ def main() -> int:
     else:
         # The gradient pass of the same problem: its inputs are the forward's O and
         # L and a seeded dO.
-        fa.forward(dq, dk, dv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        fa.forward(dq, dk, dv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream, **mask_kw)
         g = torch.Generator().manual_seed(1)
         dout_h = torch.randn((w.B, w.H, w.N, w.d), generator=g).to(q.dtype)
         dout = dout_h.cuda()
@@ -546,11 +560,17 @@ def main() -> int:
 
         def step():
             fa.backward(dq, dk, dv, o, dout, lse, causal=w.causal, scale=w.scale, stream=stream, delta=delta,
-                        dq=gq, dk=gk, dv=gv)
+                        dq=gq, dk=gk, dv=gv, **mask_kw)
         # Conventional count: five N x N x d products per (query, key) pair (S, dP,
-        # dV, dQ, dK), 2.5x the forward's.
-        flop = 2.5 * flop_count(w.B, w.H, w.N, w.d, w.causal)
-        metric = "attention bwd TFLOP/s (5 products per pair) and % of MI355X FP16/BF16 MFMA peak"
+        # dV, dQ, dK), 2.5x the forward's; under a general mask over the visible
+        # pairs.
+        if masked:
+            flop = 2.5 * 4.0 * w.B * w.H * w.d * pairs
+            metric = ("attention bwd TFLOP/s over visible pairs (general mask, 5 products per pair), % of MI355X "
+                      "FP16/BF16 MFMA peak")
+        else:
+            flop = 2.5 * flop_count(w.B, w.H, w.N, w.d, w.causal)
+            metric = "attention bwd TFLOP/s (5 products per pair) and % of MI355X FP16/BF16 MFMA peak"
 
     # The engine clock ramps up over the first tens of milliseconds of MFMA load;
     # time_steps keeps running untimed steps until the warm-up has lasted
@@ -590,10 +610,11 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the workload ...")
-        if args.pass_ == "fwd" and masked:
+        if masked:
             result["cpu_baseline"] = cpu_baseline_masked(w, q, k, v, window, args.prefix,
                                                          None if seg_host is None else seg_host.numpy(),
-                                                         mask_cfg["visible_pairs_per_head"], args.cpu_seconds)
+                                                         pairs, args.cpu_seconds,
+                                                         dout=dout_h if args.pass_ == "bwd" else None)
         elif args.pass_ == "fwd":
             result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
         else:

@@ -41,7 +41,8 @@ FA2_ERR_WORKSPACE = 11
 FA2_ERR_SCRATCH = 12
 
 # Every symbol include/fa2.h declares.
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_fwd_fp8", "fa2_bwd", "fa2_decode", "fa2_decode_static",
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_fwd_fp8", "fa2_bwd", "fa2_bwd_masked", "fa2_decode",
+                    "fa2_decode_static",
                     "fa2_decode_workspace_bytes", "fa2_clock_sample", "fa2_status_str", "fa2_last_hip_error")
 DECODE_STATIC_SCRATCH_BYTES = 4 << 20  # FA2_DECODE_STATIC_SCRATCH_BYTES
 CLOCK_BLOCKS = 2048  # FA2_CLOCK_BLOCKS
@@ -89,6 +90,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                             ctypes.c_float, ctypes.c_int, vp]
     lib.fa2_bwd.restype = ctypes.c_int
+    lib.fa2_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                   ctypes.POINTER(Fa2Mask), ctypes.c_float, ctypes.c_int, vp]
+    lib.fa2_bwd_masked.restype = ctypes.c_int
     lib.fa2_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp, vp,
                                 ctypes.c_int, vp]
     lib.fa2_fwd_fp8.restype = ctypes.c_int
@@ -130,6 +134,30 @@ def fa2_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, delta: int, dq:
     """Direct call of the gradient entry point with raw device addresses; returns the status."""
     return load_library().fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, int(causal),
                                   float(scale), int(dtype), stream)
+
+
+def fa2_bwd_masked(q: int, k: int, v: int, o: int, dout: int, lse: int, delta: int, dq: int, dk: int, dv: int,
+                   B: int, H: int, N: int, d: int, mask, scale: float, dtype: int, stream: int) -> int:
+    """Direct call of the masked gradient entry point (mask: a Fa2Mask or None)."""
+    ptr = ctypes.byref(mask) if mask is not None else None
+    return load_library().fa2_bwd_masked(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, ptr, float(scale),
+                                         int(dtype), stream)
+
+
+def _general_mask(causal, window, prefix, segment_ids, B, N, device):
+    """A Fa2Mask for a general mask, or None when there is none."""
+    import torch
+
+    if window is None and not prefix and segment_ids is None:
+        return None
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    seg_ptr = None
+    if segment_ids is not None:
+        if (segment_ids.shape != (B, N) or segment_ids.dtype != torch.int32 or not segment_ids.is_contiguous()
+                or segment_ids.device != device):
+            raise ValueError("segment_ids must be a contiguous int32 [B, N] tensor on q's device")
+        seg_ptr = segment_ids.data_ptr()
+    return Fa2Mask(int(bool(causal)), wl, wr, int(prefix), seg_ptr)
 
 
 def fa2_fwd_fp8(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, causal: int,
@@ -263,16 +291,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         raise ValueError("out must be a contiguous tensor like q")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
-    general = window is not None or prefix or segment_ids is not None
-    if general:
-        wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
-        seg_ptr = None
-        if segment_ids is not None:
-            if (segment_ids.shape != (B, N) or segment_ids.dtype != torch.int32 or not segment_ids.is_contiguous()
-                    or segment_ids.device != q.device):
-                raise ValueError("segment_ids must be a contiguous int32 [B, N] tensor on q's device")
-            seg_ptr = segment_ids.data_ptr()
-        mask = Fa2Mask(int(bool(causal)), wl, wr, int(prefix), seg_ptr)
+    mask = _general_mask(causal, window, prefix, segment_ids, B, N, q.device)
+    general = mask is not None
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         if general:
@@ -287,12 +307,13 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
 
 
 def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, stream=None,
-             delta=None, dq=None, dk=None, dv=None):
+             delta=None, dq=None, dk=None, dv=None, window=None, prefix: int = 0, segment_ids=None):
     """Gradients of attention on the GPU.  Returns ``(dq, dk, dv)``.
 
     ``o`` and ``lse`` are the forward pass's outputs for the same ``q, k, v``,
-    ``causal`` and ``scale``; ``dout`` is the gradient of the loss with respect
-    to ``o``.  ``delta`` ([B, H, N] float32) receives the row statistic
+    ``causal``, ``scale`` and mask (``window``, ``prefix``, ``segment_ids``, as
+    for ``forward``); ``dout`` is the gradient of the loss with respect to
+    ``o``.  ``delta`` ([B, H, N] float32) receives the row statistic
     D = rowsum(dout * o); it and the outputs are allocated here unless given.
     """
     import torch
@@ -323,17 +344,23 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
     if (delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous()
             or not delta.is_cuda or delta.device != q.device):
         raise ValueError("delta must be a contiguous float32 [B, H, N] tensor on q's device")
+    mask = _general_mask(causal, window, prefix, segment_ids, B, N, q.device)
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         if own_delta:
             # delta is dropped on return while the kernels may still use it on s:
             # the caching allocator must not hand its block to other streams first.
             delta.record_stream(s)
-        rc = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                     delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
-                     int(bool(causal)), float(scale), code, s.cuda_stream)
+        if mask is not None:
+            rc = fa2_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H,
+                                N, d, mask, float(scale), code, s.cuda_stream)
+        else:
+            rc = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                         delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                         int(bool(causal)), float(scale), code, s.cuda_stream)
     if rc != FA2_OK:
-        raise Fa2Error(rc, fa2_status_str(rc), "fa2_bwd")
+        raise Fa2Error(rc, fa2_status_str(rc), "fa2_bwd_masked" if mask is not None else "fa2_bwd")
     return dq, dk, dv
 
 

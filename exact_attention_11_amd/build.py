@@ -49,13 +49,14 @@ def build(out: str = LIB_PATH, verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with code {res.returncode}")
-    # MFMAs written as inline assembly are invisible to the compiler's hazard
-    # recognizer: check their spacing on the built code before installing it.
+    # MFMAs and LDS copies written as inline assembly are invisible to the
+    # compiler's hazard recognizer: check their spacing on the built code before
+    # installing it.
     from . import hazards
     bad = hazards.check_library(tmp)
     if bad:
         os.remove(tmp)
-        raise RuntimeError("MFMA hazards in the built kernels (function, kind, MFMA address, other address, "
+        raise RuntimeError("hazards in the built kernels (function, kind, first address, second address, "
                            f"wait states): {bad[:8]}")
     os.replace(tmp, out)
     return out

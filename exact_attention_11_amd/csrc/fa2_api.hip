@@ -116,7 +116,7 @@ hipError_t launch_d(const fa2::FwdArgs& args, int64_t d, int mask_mode, hipStrea
   }
 }
 
-template <int kDType, int D, bool kCausal>
+template <int kDType, int D, int kMask>
 hipError_t launch_bwd(const fa2::bwd::BwdArgs& args, hipStream_t stream) {
   using namespace fa2::bwd;
   const int64_t rows = (int64_t)args.BH * args.N;
@@ -124,23 +124,31 @@ hipError_t launch_bwd(const fa2::bwd::BwdArgs& args, hipStream_t stream) {
                      0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa2_bwd_dkdv<kDType, D, kCausal>), dim3((unsigned)(args.n_kv_wg * args.BH)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fa2_bwd_dkdv<kDType, D, kMask>), dim3((unsigned)(args.n_kv_wg * args.BH)), dim3(kThreads), 0,
                      stream, args);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa2_bwd_dq<kDType, D, kCausal>), dim3((unsigned)(args.n_q_wg * args.BH)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fa2_bwd_dq<kDType, D, kMask>), dim3((unsigned)(args.n_q_wg * args.BH)), dim3(kThreads), 0,
                      stream, args);
   return hipGetLastError();
 }
 
+template <int kDType, int D>
+hipError_t launch_bwd_m(const fa2::bwd::BwdArgs& args, int mask_mode, hipStream_t stream) {
+  switch (mask_mode) {
+    case fa2::kMaskNone: return launch_bwd<kDType, D, fa2::kMaskNone>(args, stream);
+    case fa2::kMaskCausal: return launch_bwd<kDType, D, fa2::kMaskCausal>(args, stream);
+    case fa2::kMaskGeneral: return launch_bwd<kDType, D, fa2::kMaskGeneral>(args, stream);
+    default: return launch_bwd<kDType, D, fa2::kMaskSegments>(args, stream);
+  }
+}
+
 template <int kDType>
-hipError_t launch_bwd_d(const fa2::bwd::BwdArgs& args, int64_t d, bool causal, hipStream_t stream) {
+hipError_t launch_bwd_d(const fa2::bwd::BwdArgs& args, int64_t d, int mask_mode, hipStream_t stream) {
   switch (d) {
-    case 64: return causal ? launch_bwd<kDType, 64, true>(args, stream) : launch_bwd<kDType, 64, false>(args, stream);
-    case 128:
-      return causal ? launch_bwd<kDType, 128, true>(args, stream) : launch_bwd<kDType, 128, false>(args, stream);
-    default:
-      return causal ? launch_bwd<kDType, 256, true>(args, stream) : launch_bwd<kDType, 256, false>(args, stream);
+    case 64: return launch_bwd_m<kDType, 64>(args, mask_mode, stream);
+    case 128: return launch_bwd_m<kDType, 128>(args, mask_mode, stream);
+    default: return launch_bwd_m<kDType, 256>(args, mask_mode, stream);
   }
 }
 
@@ -463,9 +471,9 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   return fa2_fwd_masked(q, k, v, o, lse, B, H, N, d, &m, scale, dtype, stream);
 }
 
-int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-            float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
-            float scale, int dtype, void* stream) {
+int fa2_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                   const fa2_mask* mask, float scale, int dtype, void* stream) {
   g_last_hip_error = 0;
   // ---- argument checks: no HIP call before they all pass -------------------
   if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
@@ -473,8 +481,12 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
   const float c2 = (float)((double)scale * 1.4426950408889634074);
   if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
+  fa2_mask m = {0, -1, -1, 0, nullptr};
+  if (mask) m = *mask;
+  if (m.window_left < -1 || m.window_right < -1 || m.prefix < 0) return FA2_ERR_MASK;
+  if (((uintptr_t)m.segment_ids) & 3) return FA2_ERR_MASK;
   if (B == 0 || H == 0 || N == 0) return FA2_OK;
-  if (N > (int64_t)INT32_MAX - 256) return FA2_ERR_SHAPE;
+  if (N > (int64_t)INT32_MAX - 65536) return FA2_ERR_SHAPE;
   if (B > INT32_MAX || H > INT32_MAX) return FA2_ERR_SHAPE;
   const int64_t bh = B * H;
   const int64_t n_kv = (N + fa2::bwd::kKeysPerWg - 1) / fa2::bwd::kKeysPerWg;
@@ -497,6 +509,25 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const vo
       if (overlaps(out[i], out_n[i], in[j], in_n[j])) return FA2_ERR_ALIAS;
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(out[i], out_n[i], out[j], out_n[j])) return FA2_ERR_ALIAS;
+    if (m.segment_ids && overlaps(out[i], out_n[i], m.segment_ids, (uint64_t)(B * N) * 4)) return FA2_ERR_ALIAS;
+  }
+
+  // ---- mask: as in fa2_fwd_masked (the forward that produced lse must have
+  // used the same mask) --------------------------------------------------------
+  int64_t wl = m.window_left, wr = m.window_right, prefix = m.prefix;
+  if (m.causal) wr = 0;
+  if (wl >= N - 1) wl = -1;
+  if (wr >= N - 1) wr = -1;
+  if (prefix >= N) {
+    wl = -1;
+    wr = -1;
+    prefix = 0;
+  }
+  if (wl < 0 && wr < 0) prefix = 0;
+  int mode = m.segment_ids ? fa2::kMaskSegments : fa2::kMaskGeneral;
+  if (!m.segment_ids && prefix == 0 && wl < 0) {
+    if (wr < 0) mode = fa2::kMaskNone;
+    else if (wr == 0) mode = fa2::kMaskCausal;
   }
 
   // ---- device ---------------------------------------------------------------
@@ -520,15 +551,26 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   args.n_q_wg = (int)n_q;
   args.scale = scale;
   args.c2 = c2;
+  args.wl = (int)wl;
+  args.wr = (int)wr;
+  args.prefix = (int)prefix;
+  args.H = (int)H;
+  args.seg = m.segment_ids;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_bwd_d<0>(args, d, causal != 0, s)
-                                         : launch_bwd_d<1>(args, d, causal != 0, s);
+  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_bwd_d<0>(args, d, mode, s) : launch_bwd_d<1>(args, d, mode, s);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FA2_ERR_LAUNCH;
   }
   return FA2_OK;
+}
+
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+            float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+            float scale, int dtype, void* stream) {
+  const fa2_mask m = {causal, -1, -1, 0, nullptr};
+  return fa2_bwd_masked(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, &m, scale, dtype, stream);
 }
 
 int64_t fa2_decode_workspace_bytes(int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d) {

@@ -79,6 +79,14 @@ struct BwdArgs {
   int n_q_wg;   // ceil(N / kRowsPerWg)
   float scale;  // multiplier of the scores
   float c2;     // scale * log2(e)
+  // General mask (the kMaskGeneral and kMaskSegments instances): key c is
+  // visible to query r iff c < N, seg[b, c] == seg[b, r] (segment instances),
+  // and c < prefix or r - wl <= c <= r + wr (a negative bound is no bound).
+  int wl;
+  int wr;
+  int prefix;
+  int H;           // heads per batch: batch b = (b*H + h) / H
+  const int* seg;  // [B, N] segment ids, or nullptr
 };
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -102,11 +110,33 @@ template <int D> __device__ __forceinline__ uint32_t tile_byte(int row, int chun
   return (uint32_t)(row * D * 2 + ((chunk ^ swz<D>(row)) << 4));
 }
 
+// A wave-uniform address that the compiler holds in VGPRs (it came through
+// LDS or a local argument block), moved into SGPRs for the scalar base of dma16_sbase: v_readfirstlane of
+// each half (the builtin returns int: back to uint32_t before the halves are
+// joined, or bit 31 of the low half would sign-extend over the high half),
+// then the 5 wait states that a vector memory instruction reading an SGPR needs
+// after a VALU instruction wrote it.  The compiler keeps that distance before
+// its own memory instructions, but cannot see that the copies (inline asm) read
+// SGPRs.  The s_nop reads both halves, so it follows their writes, and as a
+// volatile asm statement it stays ahead of the copies (volatile too).  (The
+// halves do not pass through the asm as outputs: the compiler would no longer
+// know they are uniform.)
+__device__ __forceinline__ const void* sgpr_base(const void* p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+  asm volatile("s_nop 4" ::"s"(lo), "s"(hi));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
 // Copy R rows (r0.., clamped to N - 1) of a [N, D] head into an LDS tile; each
 // instruction of a wave fills 64 consecutive 16-byte slots.  Addressed as the
 // wave-uniform row r0 plus a 32-bit per-lane offset, so that no per-lane 64-bit
-// address stays live across the kernel's loop.
-template <int D, int R>
+// address stays live across the kernel's loop.  kVBase: r0 is uniform but the
+// compiler cannot prove it (the general-mask kernels' tile bounds, which pass
+// through an LDS reduction under segment ids and through a local argument
+// block otherwise), so the base goes to scalar registers through sgpr_base.
+template <int D, int R, bool kVBase = false>
 __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2_LDS uint16_t* dst, int r0, int N,
                                           int wave, int lane) {
   constexpr int CPR = D / 8;
@@ -114,6 +144,7 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2
   constexpr int kStride = 64 * kWaves / CPR;  // rows between a wave's consecutive copies
   static_assert(kPer * 64 * kWaves == R * CPR, "tile copy split");
   const uint16_t* base = head + (int64_t)r0 * D;
+  if constexpr (kVBase) base = (const uint16_t*)sgpr_base(base);
   const int last = N - 1 - r0;  // rows past it re-read row N - 1
   // From d = 128 on, the lane index as a value the compiler cannot see
   // through: the per-copy offsets below are then formed here, at each call,
@@ -179,8 +210,11 @@ __global__ __launch_bounds__(256) void fa2_bwd_delta(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dK and dV of kKeysPerWg keys of one head; query tiles stream through LDS.
-template <int kDType, int D, bool kCausal>
+template <int kDType, int D, int kMask>
 __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArgs a) {
+  constexpr bool kCausal = kMask == kMaskCausal;
+  constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
+  constexpr bool kSeg = kMask == kMaskSegments;
   typedef Elem<kDType> E;
   typedef typename E::V8 V8;
   constexpr int KS = D / 16;  // k-steps of S = Q K^T over the head dim
@@ -193,13 +227,15 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
   constexpr int QT = kVLds ? 32 : kQTile;  // query rows per streamed tile
   constexpr int kTile = QT * D;
   constexpr int kStat = 64;  // floats per L or D row of the stat buffers (one copy of 64 lanes)
+  constexpr int kNStat = kSeg ? 3 : 2;  // stat rows per buffer: L, D (and the rows' segment ids)
   // Operand offsets formed at each use from a few lane values (below) from
   // d = 128 on, where holding all of them across the loop costs spills.
   constexpr bool kXorAddr = D >= 128;
 
   // [buffer][Q | dO] tiles, then [buffer][L | D] rows.
   __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];
-  __shared__ __attribute__((aligned(1024))) float stat_[2][2][kStat];
+  __shared__ __attribute__((aligned(1024))) float stat_[2][kNStat][kStat];
+  __shared__ int red_[2 * kWaves];  // segment span reduction
   __shared__ __attribute__((aligned(1024))) uint16_t vt_[kVLds ? kKeysPerWg * D : 8];
   FA2_LDS uint16_t* const sT = (FA2_LDS uint16_t*)smem_;
   FA2_LDS float* const sS = (FA2_LDS float*)&stat_[0][0][0];
@@ -223,23 +259,47 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
   const uint16_t* __restrict__ gh = a.dout + head_off;
   const float* __restrict__ lh = a.lse + (int64_t)bh * N;
   const float* __restrict__ dh = a.delta + (int64_t)bh * N;
+  const int* __restrict__ segb = kSeg ? a.seg + (int64_t)(bh / a.H) * N : nullptr;
 
-  const int it0 = kCausal ? (kt * kKeysPerWg) / QT : 0;  // first query tile that sees these keys
-  const int it1 = (N + QT - 1) / QT;
+  // Query tiles that see these keys: under the causal mask those from the
+  // keys' own tile on; under a general mask the rows whose window reaches the
+  // keys (every row when a key lies in the prefix), narrowed under segment ids
+  // to the rows whose ids lie between the keys' least and greatest id.
+  int it0 = kCausal ? (kt * kKeysPerWg) / QT : 0;
+  int it1 = (N + QT - 1) / QT;
+  if constexpr (kGeneral) {
+    const int k0 = kt * kKeysPerWg, k1 = min(N - 1, k0 + kKeysPerWg - 1);
+    int lo = 0, hi = N - 1;
+    if (k0 >= a.prefix) {
+      if (a.wr >= 0) lo = max(0, k0 - a.wr);
+      if (a.wl >= 0) hi = min(N - 1, k1 + a.wl);
+    }
+    if constexpr (kSeg) {
+      int f, l;
+      segment_span<kWaves>(segb, k0, k1, lo, hi, (FA2_LDS int*)red_, f, l);
+      lo = max(lo, f);
+      hi = min(hi, l);
+    }
+    it0 = lo / QT;
+    it1 = hi / QT + 1;
+  }
 
   auto load_tile = [&](int it, int buf) __attribute__((always_inline)) {
-    load_rows<D, QT>(qh, sT + (2 * buf + 0) * kTile, it * QT, N, wave, lane);
-    load_rows<D, QT>(gh, sT + (2 * buf + 1) * kTile, it * QT, N, wave, lane);
+    load_rows<D, QT, kGeneral>(qh, sT + (2 * buf + 0) * kTile, it * QT, N, wave, lane);
+    load_rows<D, QT, kGeneral>(gh, sT + (2 * buf + 1) * kTile, it * QT, N, wave, lane);
     if (wave == 0) {
       const int r = min(it * QT + lane, N - 1);
-      dma4(lh + r, sS + (2 * buf + 0) * kStat);
-      dma4(dh + r, sS + (2 * buf + 1) * kStat);
+      dma4(lh + r, sS + (kNStat * buf + 0) * kStat);
+      dma4(dh + r, sS + (kNStat * buf + 1) * kStat);
+      if constexpr (kSeg) dma4(segb + r, sS + (kNStat * buf + 2) * kStat);
     }
   };
   // V of the workgroup's keys (d = 256), complete at the loop's first barrier.
-  if constexpr (kVLds) load_rows<D, kKeysPerWg>(a.v + head_off, sV, kt * kKeysPerWg, N, wave, lane);
+  if constexpr (kVLds) load_rows<D, kKeysPerWg, kGeneral>(a.v + head_off, sV, kt * kKeysPerWg, N, wave, lane);
   load_tile(it0, 0);
 
+  // The segment id of this lane's key.
+  const int seg_k = kSeg ? segb[min(my_k, N - 1)] : 0;
   // K and V of this lane's key (B operands of S = Q K^T and dP = dO V^T).
   V8 kf[KS], vf[kVLds ? 1 : KS];
   {
@@ -272,13 +332,18 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
     if (it + 1 < it1) load_tile(it + 1, buf ^ 1);
     const FA2_LDS uint16_t* tq = sT + (2 * buf + 0) * kTile;
     const FA2_LDS uint16_t* tg_ = sT + (2 * buf + 1) * kTile;
-    const FA2_LDS float* tL = sS + (2 * buf + 0) * kStat;
-    const FA2_LDS float* tD = sS + (2 * buf + 1) * kStat;
+    const FA2_LDS float* tL = sS + (kNStat * buf + 0) * kStat;
+    const FA2_LDS float* tD = sS + (kNStat * buf + 1) * kStat;
+    const FA2_LDS int* tG = (const FA2_LDS int*)(sS + (kNStat * buf + (kSeg ? 2 : 0)) * kStat);
 #pragma unroll
     for (int sb = 0; sb < QT / 32; ++sb) {
       const int q0 = it * QT + sb * 32;
       if (q0 >= N) break;
       if (kCausal && q0 + 31 < kw0) continue;  // every query precedes every key of this wave
+      // (wave-uniform) no query of these 32 rows sees a key of this wave
+      if (kGeneral && kw0 >= a.prefix &&
+          ((a.wr >= 0 && kw0 > q0 + 31 + a.wr) || (a.wl >= 0 && kw0 + 31 < q0 - a.wl)))
+        continue;
       // LDS byte offsets of this lane's operand reads.  Row reads (row r of a
       // tile, chunk 2 ks + hl): the swizzle depends on r % 16 only, and
       // (2 ks + hl) ^ z = 2 ks ^ (hl ^ z), so chunk ks sits at
@@ -316,7 +381,7 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
       }
       // Element e of the accumulators is query q0 + 8*(e/4) + 4*hl + e%4 of this
       // lane's key; its L and D sit at the same offset in the stat rows.
-      const bool need_mask = (q0 + 32 > N) || (kCausal && kw0 + 31 > q0);
+      const bool need_mask = kGeneral || (q0 + 32 > N) || (kCausal && kw0 + 31 > q0);
       const int lim_n = N - q0 - 4 * hl;          // query < N      <=> qi < lim_n
       const int lim_c = my_k - q0 - 4 * hl;       // key <= query   <=> qi >= lim_c
       uint32_t pp[2][4], pd[2][4];                // P and dS packed, per 16-query k-step
@@ -324,6 +389,8 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
       for (int g = 0; g < 4; ++g) {
         const u32x4 lw = *(const FA2_LDS u32x4*)(tL + sb * 32 + 8 * g + 4 * hl);
         const u32x4 dw = *(const FA2_LDS u32x4*)(tD + sb * 32 + 8 * g + 4 * hl);
+        u32x4 sq = {0u, 0u, 0u, 0u};
+        if constexpr (kSeg) sq = *(const FA2_LDS u32x4*)(tG + sb * 32 + 8 * g + 4 * hl);
         float p[4], ds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -331,7 +398,12 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
           float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c2, -__uint_as_float(lw[i]) * kLog2e));
           if (need_mask) {
             const int qi = 8 * g + i;
-            const bool ok = qi < lim_n && (!kCausal || qi >= lim_c);
+            bool ok = qi < lim_n && (!kCausal || qi >= lim_c);
+            if constexpr (kGeneral) {
+              const int qa = q0 + 4 * hl + qi;  // the query of this element
+              ok = ok && (my_k < a.prefix || ((a.wl < 0 || my_k >= qa - a.wl) && (a.wr < 0 || my_k <= qa + a.wr)));
+              if constexpr (kSeg) ok = ok && (int)sq[i] == seg_k;
+            }
             x = ok ? x : 0.f;
           }
           p[i] = x;
@@ -398,8 +470,11 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
 
 // ---------------------------------------------------------------------------
 // dQ of kRowsPerWg query rows of one head; key/value tiles stream through LDS.
-template <int kDType, int D, bool kCausal>
+template <int kDType, int D, int kMask>
 __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a) {
+  constexpr bool kCausal = kMask == kMaskCausal;
+  constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
+  constexpr bool kSeg = kMask == kMaskSegments;
   typedef Elem<kDType> E;
   typedef typename E::V8 V8;
   constexpr int KS = D / 16;
@@ -411,6 +486,8 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];  // [buffer][K | V]
   FA2_LDS uint16_t* const sT = (FA2_LDS uint16_t*)smem_;
+  __shared__ __attribute__((aligned(16))) int segk_[kSeg ? 2 * 64 : 4];  // [buffer] the keys' segment ids
+  __shared__ int red_[2 * kWaves];                                      // segment span reduction
 
   const int N = a.N;
   // Under the causal mask the last query tiles see the most keys: dispatch
@@ -430,12 +507,46 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
   const uint16_t* __restrict__ kh = a.k + head_off;
   const uint16_t* __restrict__ vh = a.v + head_off;
 
-  const int kv_end = kCausal ? min(N, (qt + 1) * kRowsPerWg) : N;
-  const int nt = (kv_end + KT - 1) / KT;
+  const int* __restrict__ segb = kSeg ? a.seg + (int64_t)(bh / a.H) * N : nullptr;
+
+  // Key tiles: step j visits tile tile_of(j), j < nt.  Without a general mask
+  // tiles 0 .. nt-1 (under the causal mask up to the rows' last key); a general
+  // mask visits the runs of key tiles the forward pass visits (the prefix, the
+  // window), cut under segment ids to the keys whose ids can match.
+  int nt, run_a0 = 0, run_na = 0, run_b0 = 0;
+  if constexpr (kGeneral) {
+    const int q0 = qt * kRowsPerWg, q1 = min(N, q0 + kRowsPerWg) - 1;
+    FwdArgs m{};
+    m.N = N;
+    m.wl = a.wl;
+    m.wr = a.wr;
+    m.prefix = a.prefix;
+    int kf = 0, kl = N - 1;
+    if constexpr (kSeg) {
+      const TileRuns all = general_runs(m, q0, q1, 0, N - 1, KT);
+      const int lo = all.na > 0 ? 0 : all.b0 * KT;
+      const int hi = min(N - 1, (all.b0 + all.nb) * KT - 1);
+      segment_span<kWaves>(segb, q0, q1, lo, hi, (FA2_LDS int*)red_, kf, kl);
+    }
+    const TileRuns r = general_runs(m, q0, q1, kf, kl, KT);
+    run_a0 = r.a0;
+    run_na = r.na;
+    run_b0 = r.b0;
+    nt = r.na + r.nb;
+  } else {
+    const int kv_end = kCausal ? min(N, (qt + 1) * kRowsPerWg) : N;
+    nt = (kv_end + KT - 1) / KT;
+  }
+  auto tile_of = [&](int j) __attribute__((always_inline)) {
+    if constexpr (kGeneral) return j < run_na ? run_a0 + j : run_b0 + (j - run_na);
+    else return j;
+  };
 
   auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
-    load_rows<D, KT>(kh, sT + (2 * buf + 0) * kTile, j * KT, N, wave, lane);
-    load_rows<D, KT>(vh, sT + (2 * buf + 1) * kTile, j * KT, N, wave, lane);
+    const int kv0 = tile_of(j) * KT;
+    load_rows<D, KT, kGeneral>(kh, sT + (2 * buf + 0) * kTile, kv0, N, wave, lane);
+    load_rows<D, KT, kGeneral>(vh, sT + (2 * buf + 1) * kTile, kv0, N, wave, lane);
+    if (kSeg && wave == 0) dma4(segb + min(kv0 + lane, N - 1), (FA2_LDS int*)segk_ + buf * 64);
   };
   load_tile(0, 0);
 
@@ -454,6 +565,7 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
   }
   const float l2 = a.lse[(int64_t)bh * N + rq] * kLog2e;
   const float dd = a.delta[(int64_t)bh * N + rq];
+  const int seg_q = kSeg ? segb[rq] : 0;
 
   f32x16 dqt[DB];  // dQ^T: rows = head dim, columns = this wave's queries
 #pragma unroll
@@ -466,8 +578,11 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
     const int buf = j & 1;
     wait_vm_lds_barrier<0>();
     if (j + 1 < nt) load_tile(j + 1, buf ^ 1);
-    const int kv0 = j * KT;
-    const bool active = !kCausal || kv0 <= q_row0 + 31;
+    const int kv0 = tile_of(j) * KT;
+    bool active = !kCausal || kv0 <= q_row0 + 31;
+    if constexpr (kGeneral)
+      active = !(kv0 >= a.prefix && ((a.wr >= 0 && kv0 > q_row0 + 31 + a.wr) ||
+                                     (a.wl >= 0 && kv0 + KT - 1 < q_row0 - a.wl)));
     if (!active) continue;  // wave-uniform; the barriers stay in step
     const FA2_LDS uint16_t* tk = sT + (2 * buf + 0) * kTile;
     const FA2_LDS uint16_t* tv = sT + (2 * buf + 1) * kTile;
@@ -487,20 +602,27 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
       }
     }
     // Element (kb, e) is key kv0 + 32*kb + 8*(e/4) + 4*hl + e%4 of query my_q.
-    const bool need_mask = (kv0 + KT > N) || (kCausal && kv0 + KT - 1 > q_row0);
+    const bool need_mask = kGeneral || (kv0 + KT > N) || (kCausal && kv0 + KT - 1 > q_row0);
     const int base = kv0 + 4 * hl;
+    const FA2_LDS int* tsg = (const FA2_LDS int*)segk_ + buf * 64;
     uint32_t pd[KT / 32][8];
 #pragma unroll
     for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
         float ds2[2];
+        u32x2 sk = {0u, 0u};
+        if constexpr (kSeg) sk = *(const FA2_LDS u32x2*)(tsg + 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3));
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + i], a.c2, -l2));
           if (need_mask) {
             const int key = base + 32 * kb + 8 * ((e + i) >> 2) + ((e + i) & 3);
-            const bool ok = key < N && (!kCausal || key <= my_q);
+            bool ok = key < N && (!kCausal || key <= my_q);
+            if constexpr (kGeneral) {
+              ok = ok && (key < a.prefix || ((a.wl < 0 || key >= my_q - a.wl) && (a.wr < 0 || key <= my_q + a.wr)));
+              if constexpr (kSeg) ok = ok && (int)sk[i] == seg_q;
+            }
             x = ok ? x : 0.f;
           }
           ds2[i] = x * (dp[kb][e + i] - dd);

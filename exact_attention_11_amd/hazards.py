@@ -1,16 +1,19 @@
-"""Build-time check of MFMA hazards that the compiler cannot see.
+"""Build-time check of instruction hazards that the compiler cannot see.
 
-Some kernels issue MFMAs as inline assembly (to keep their accumulators in
-vector registers).  The compiler's hazard recognizer does not know these
-instructions are MFMAs, so this module checks the library's own gfx950 code
-object (disassembled with llvm-objdump) along every control-flow path:
+Some kernels issue MFMAs and LDS copies (global_load_lds) as inline assembly.
+The compiler's hazard recognizer does not know what these instructions are, so
+this module checks the library's own gfx950 code object (disassembled with
+llvm-objdump) along every control-flow path:
 
 * result hazard: a non-MFMA vector, LDS or global instruction that reads or
   writes a VGPR an MFMA wrote must come at least RESULT_WAITS wait states after
   that MFMA (an MFMA that rewrites exactly the same registers as its
   accumulator, the in-place accumulation form, is exempt);
 * operand hazard: an MFMA must come at least OPERAND_WAITS wait states after a
-  vector ALU instruction that wrote any VGPR it reads.
+  vector ALU instruction that wrote any VGPR it reads;
+* SGPR hazard (every kernel): a vector memory instruction that reads an SGPR
+  (a scalar base address) must come at least SGPR_VMEM_WAITS wait states after
+  a vector ALU instruction that wrote that SGPR (v_readfirstlane and the like).
 
 Each instruction counts as one wait state and ``s_nop N`` as N + 1, which never
 overstates the hardware's count.  RESULT_WAITS covers the longest (16-pass)
@@ -26,6 +29,7 @@ import tempfile
 
 RESULT_WAITS = 19
 OPERAND_WAITS = 2
+SGPR_VMEM_WAITS = 5
 LLVM_BIN = "/opt/rocm/llvm/bin"
 TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
 
@@ -33,11 +37,18 @@ _INSN = re.compile(r"^\s+(\S+)(.*?)\s*//\s*([0-9A-Fa-f]+):")
 _TGT = re.compile(r"<([^>+]+)\+0x([0-9a-f]+)>")
 _FUNC = re.compile(r"^([0-9a-f]+) <([^>]+)>:")
 _VREG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
+_SREG = re.compile(r"\bs\[(\d+):(\d+)\]|\bs(\d+)\b")
+# Vector ALU instructions that write an SGPR: the first operand of these ...
+_SGPR_DST_FIRST = ("v_readfirstlane", "v_readlane", "v_cmp_", "v_cmpx_")
+# ... and the second (carry-out or flag) operand of these.
+_SGPR_DST_SECOND = ("v_add_co_", "v_sub_co_", "v_subrev_co_", "v_addc_co_", "v_subb_co_", "v_subbrev_co_",
+                    "v_div_scale_", "v_mad_u64_u32", "v_mad_i64_i32")
+_VMEM = ("global_", "buffer_", "scratch_", "flat_")
 
 
-def _vregs(text: str) -> set:
+def _regs(pattern, text: str) -> set:
     out = set()
-    for m in _VREG.finditer(text):
+    for m in pattern.finditer(text):
         if m.group(3) is not None:
             out.add(int(m.group(3)))
         else:
@@ -45,8 +56,21 @@ def _vregs(text: str) -> set:
     return out
 
 
+def _vregs(text: str) -> set:
+    return _regs(_VREG, text)
+
+
+def _sgpr_writes(op: str, operands: str) -> set:
+    args = [a.strip() for a in operands.split(",")]
+    if op.startswith(_SGPR_DST_FIRST) and args:
+        return _regs(_SREG, args[0])
+    if op.startswith(_SGPR_DST_SECOND) and len(args) > 1:
+        return _regs(_SREG, args[1])
+    return set()
+
+
 class Insn:
-    __slots__ = ("addr", "op", "dst", "src", "text", "waits", "target")
+    __slots__ = ("addr", "op", "dst", "src", "text", "waits", "target", "sdst", "ssrc")
 
     def __init__(self, addr: int, op: str, operands: str, target):
         self.addr, self.op, self.text, self.target = addr, op, operands, target
@@ -57,6 +81,9 @@ class Insn:
         for a in args[1:] if writes_first else args:
             self.src |= _vregs(a)
         self.waits = int(operands.split()[0], 0) + 1 if op == "s_nop" else 1
+        # SGPRs a vector ALU instruction writes; SGPRs a vector memory instruction reads
+        self.sdst = _sgpr_writes(op, operands) if op.startswith("v_") else set()
+        self.ssrc = _regs(_SREG, operands) if op.startswith(_VMEM) else set()
 
 
 def parse(dis: str) -> dict:
@@ -103,8 +130,31 @@ def _accumulates_in_place(mfma, other) -> bool:
     return len(args) == 4 and _vregs(args[0]) == mfma.dst and _vregs(args[3]) == mfma.dst
 
 
+def check_sgpr_function(insns) -> list:
+    """SGPR hazards in one function: ("sgpr", writer address, memory instruction
+    address, wait states between them)."""
+    succ = _successors(insns)
+    bad = []
+    for i, ins in enumerate(insns):
+        if not ins.sdst:
+            continue
+        seen = set()
+        stack = [(j, 0) for j in succ[i]]
+        while stack:
+            j, w = stack.pop()
+            if w >= SGPR_VMEM_WAITS or (j, w) in seen:
+                continue
+            seen.add((j, w))
+            o = insns[j]
+            if o.ssrc & ins.sdst:
+                bad.append(("sgpr", ins.addr, o.addr, w))
+                continue
+            stack.extend((k, w + o.waits) for k in succ[j])
+    return bad
+
+
 def check_function(insns) -> list:
-    """Violations in one function: (kind, mfma address, other address, wait states)."""
+    """MFMA hazards in one function: (kind, mfma address, other address, wait states)."""
     succ = _successors(insns)
     pred = [[] for _ in insns]
     for i, s in enumerate(succ):
@@ -170,7 +220,8 @@ def disassemble(lib: str) -> str:
 
 
 def check_library(lib: str, pattern: str = "fa2_fwd_w64") -> list:
-    """Violations in every kernel of lib whose name contains pattern."""
+    """MFMA hazards in every kernel of lib whose name contains pattern (those
+    that issue MFMAs as inline assembly) and SGPR hazards in every kernel."""
     funcs = parse(disassemble(lib))
     out = []
     names = [n for n in funcs if pattern in n]
@@ -178,4 +229,6 @@ def check_library(lib: str, pattern: str = "fa2_fwd_w64") -> list:
         raise RuntimeError(f"no kernel matching {pattern!r} in {lib}")
     for n in names:
         out += [(n,) + b for b in check_function(funcs[n])]
+    for n, insns in funcs.items():
+        out += [(n,) + b for b in check_sgpr_function(insns)]
     return out

@@ -164,6 +164,25 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const vo
             int causal, float scale, int dtype, void* stream);
 
 /*
+ * fa2_bwd_masked -- fa2_bwd under a general mask (NULL: no mask): the
+ * gradients of fa2_fwd_masked for the same mask, which must be the one the
+ * forward pass that produced o and lse used.  Masked pairs have P = 0 and so
+ * contribute to no gradient (the mask is a 0 / -inf term added to the scores:
+ * "Flash Attention 2", section "Causal masking").  Arguments, layout,
+ * ownership and errors as for fa2_bwd, plus FA2_ERR_MASK (as for
+ * fa2_fwd_masked); segment_ids must not overlap delta, dq, dk or dv.
+ * fa2_bwd(..., causal, ...) is this call with {causal, -1, -1, 0, NULL}.
+ *  - The key/value tiles a workgroup visits are cut to those some pair of which
+ *    is visible (the window's reach, the prefix, and under segment ids the span
+ *    of matching ids), as in the forward pass; pairs inside a visited tile are
+ *    masked element by element.
+ */
+int fa2_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* delta, void* dq, void* dk, void* dv,
+                   int64_t B, int64_t H, int64_t N, int64_t d,
+                   const fa2_mask* mask, float scale, int dtype, void* stream);
+
+/*
  * fa2_decode -- enqueue decode against a key/value cache on `stream` and return
  * without waiting: Mq new query rows per (batch, head) attend to the first
  * len_b rows of the cache of their (batch, head), len_b = seqlens[b] (clamped

@@ -168,6 +168,48 @@ def test_python_backward_rejects_bad_tensors(lib):
         fa.backward(q, q, q, q, q.float(), lse)
 
 
+# --- fa2_bwd_masked ---------------------------------------------------------------
+
+def _bwd_masked(mask, B=1, H=1, N=16, d=64, scale=0.125, dtype=0, delta=DL, dq=DQ, dk=DK, dv=DV):
+    return fa.fa2_bwd_masked(Q, K, V, O, DO, L, delta, dq, dk, dv, B, H, N, d, mask, scale, dtype, None)
+
+
+@pytest.mark.parametrize("fields,code", [
+    (dict(window_left=-2), fa.FA2_ERR_MASK), (dict(window_right=-5), fa.FA2_ERR_MASK),
+    (dict(prefix=-1), fa.FA2_ERR_MASK), (dict(segment_ids=0x60000002), fa.FA2_ERR_MASK),
+    (dict(segment_ids=DQ + 64), fa.FA2_ERR_ALIAS), (dict(segment_ids=DL), fa.FA2_ERR_ALIAS),
+    (dict(segment_ids=DV + 1024), fa.FA2_ERR_ALIAS),
+])
+def test_bwd_masked_argument_checks(lib, fields, code):
+    m = fa.Fa2Mask(0, -1, -1, 0, None)
+    for k_, v_ in fields.items():
+        setattr(m, k_, v_)
+    assert _bwd_masked(m) == code
+
+
+def test_bwd_masked_shared_checks(lib):
+    # the checks fa2_bwd makes apply to the masked entry as well
+    m = fa.Fa2Mask(1, 4, 0, 2, None)
+    assert _bwd_masked(m, d=32) == fa.FA2_ERR_HEADDIM
+    assert _bwd_masked(m, dtype=2) == fa.FA2_ERR_DTYPE
+    assert _bwd_masked(m, dq=Q) == fa.FA2_ERR_ALIAS
+    assert _bwd_masked(m, delta=DL + 4) == fa.FA2_ERR_ALIGN
+
+
+def test_bwd_masked_empty_problem_and_null_mask(lib):
+    assert _bwd_masked(fa.Fa2Mask(1, 3, 0, 2, None), B=0) == fa.FA2_OK
+    assert _bwd_masked(None, N=0) == fa.FA2_OK
+
+
+def test_bwd_masked_valid_call_without_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    for mask in (None, fa.Fa2Mask(1, 5, 0, 3, 0xB0000000), fa.Fa2Mask(0, 7, 2, 0, None)):
+        for d in (64, 128, 256):
+            assert _bwd_masked(mask, d=d, N=333) == fa.FA2_ERR_DEVICE
+
+
 # --- fa2_fwd_masked ----------------------------------------------------------------
 
 def _masked(mask, B=1, H=1, N=16, d=64, scale=0.125, dtype=0, o=O, lse=L):

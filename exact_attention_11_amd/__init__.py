@@ -41,8 +41,8 @@ FA2_ERR_WORKSPACE = 11
 FA2_ERR_SCRATCH = 12
 
 # Every symbol include/fa2.h declares.
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_fwd_fp8", "fa2_bwd", "fa2_bwd_masked", "fa2_decode",
-                    "fa2_decode_static",
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_masked", "fa2_fwd_fp8", "fa2_fwd_fp8_masked", "fa2_bwd", "fa2_bwd_masked",
+                    "fa2_decode", "fa2_decode_static",
                     "fa2_decode_workspace_bytes", "fa2_clock_sample", "fa2_status_str", "fa2_last_hip_error")
 DECODE_STATIC_SCRATCH_BYTES = 4 << 20  # FA2_DECODE_STATIC_SCRATCH_BYTES
 CLOCK_BLOCKS = 2048  # FA2_CLOCK_BLOCKS
@@ -96,6 +96,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp, vp,
                                 ctypes.c_int, vp]
     lib.fa2_fwd_fp8.restype = ctypes.c_int
+    lib.fa2_fwd_fp8_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.POINTER(Fa2Mask), ctypes.c_float,
+                                       vp, vp, ctypes.c_int, vp]
+    lib.fa2_fwd_fp8_masked.restype = ctypes.c_int
     lib.fa2_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                ctypes.c_int, vp, i64, vp]
     lib.fa2_decode.restype = ctypes.c_int
@@ -158,6 +161,14 @@ def _general_mask(causal, window, prefix, segment_ids, B, N, device):
             raise ValueError("segment_ids must be a contiguous int32 [B, N] tensor on q's device")
         seg_ptr = segment_ids.data_ptr()
     return Fa2Mask(int(bool(causal)), wl, wr, int(prefix), seg_ptr)
+
+
+def fa2_fwd_fp8_masked(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, mask,
+                       scale: float, descale_q: int | None, descale_k: int | None, dtype: int, stream: int) -> int:
+    """Direct call of the masked fp8 forward entry point (mask: a Fa2Mask or None)."""
+    ptr = ctypes.byref(mask) if mask is not None else None
+    return load_library().fa2_fwd_fp8_masked(q, k, v, o, lse, B, H, N, d, ptr, float(scale), descale_q, descale_k,
+                                             int(dtype), stream)
 
 
 def fa2_fwd_fp8(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, causal: int,
@@ -459,11 +470,12 @@ def decode_static(q, k, v, seqlens=None, causal: bool = False, scale: float | No
 
 
 def forward_fp8(q8, k8, v, descale_q=None, descale_k=None, causal: bool = False, scale: float | None = None,
-                out=None, lse=None, stream=None):
+                out=None, lse=None, stream=None, window=None, prefix: int = 0, segment_ids=None):
     """Attention forward with Q and K in fp8 (``torch.float8_e4m3fn``, [B, H, N,
     128]) and V in fp16 or bf16.  The real inputs are ``q8 * descale_q[b*H + h]``
     and ``k8 * descale_k[b*H + h]`` (``descale_*``: float32 [B*H] device tensors,
-    or None for ones).  Returns ``(o, lse)`` with ``o`` in V's dtype."""
+    or None for ones).  ``window``, ``prefix`` and ``segment_ids`` give a general
+    mask, as for ``forward``.  Returns ``(o, lse)`` with ``o`` in V's dtype."""
     import torch
 
     if not (q8.shape == k8.shape == v.shape) or q8.dim() != 4:
@@ -491,11 +503,16 @@ def forward_fp8(q8, k8, v, descale_q=None, descale_k=None, causal: bool = False,
         raise ValueError("out must be a contiguous tensor like v")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != v.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on the inputs' device")
+    mask = _general_mask(causal, window, prefix, segment_ids, B, N, v.device)
     with torch.cuda.device(v.device):
         s = stream if stream is not None else torch.cuda.current_stream(v.device)
-        rc = fa2_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
-                         int(bool(causal)), float(scale), ptrs[0], ptrs[1], code, s.cuda_stream)
+        if mask is not None:
+            rc = fa2_fwd_fp8_masked(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                    N, d, mask, float(scale), ptrs[0], ptrs[1], code, s.cuda_stream)
+        else:
+            rc = fa2_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                             int(bool(causal)), float(scale), ptrs[0], ptrs[1], code, s.cuda_stream)
     if rc != FA2_OK:
-        raise Fa2Error(rc, fa2_status_str(rc), "fa2_fwd_fp8")
+        raise Fa2Error(rc, fa2_status_str(rc), "fa2_fwd_fp8_masked" if mask is not None else "fa2_fwd_fp8")
     return out, lse
 

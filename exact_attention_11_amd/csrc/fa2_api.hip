@@ -55,6 +55,52 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// The caller's mask (NULL: none) after its checks: FA2_OK or FA2_ERR_MASK.
+int read_mask(const fa2_mask* mask, fa2_mask& m) {
+  m = {0, -1, -1, 0, nullptr};
+  if (mask) m = *mask;
+  if (m.window_left < -1 || m.window_right < -1 || m.prefix < 0) return FA2_ERR_MASK;
+  if (((uintptr_t)m.segment_ids) & 3) return FA2_ERR_MASK;
+  return FA2_OK;
+}
+
+// A mask as the kernels take it: the causal flag folded into the right bound,
+// bounds that cannot bite dropped, and the instance's mask mode.
+struct FoldedMask {
+  int64_t wl, wr, prefix;
+  int mode;
+};
+FoldedMask fold_mask(const fa2_mask& m, int64_t N) {
+  FoldedMask f = {m.window_left, m.window_right, m.prefix, fa2::kMaskGeneral};
+  if (m.causal) f.wr = 0;       // key <= query, whatever right bound was given
+  if (f.wl >= N - 1) f.wl = -1;  // r - wl <= 0 for every row
+  if (f.wr >= N - 1) f.wr = -1;
+  if (f.prefix >= N) {  // every key is in the prefix: the window no longer matters
+    f.wl = -1;
+    f.wr = -1;
+    f.prefix = 0;
+  }
+  if (f.wl < 0 && f.wr < 0) f.prefix = 0;  // the window admits every key already
+  if (m.segment_ids) {
+    f.mode = fa2::kMaskSegments;
+  } else if (f.prefix == 0 && f.wl < 0) {
+    if (f.wr < 0) f.mode = fa2::kMaskNone;
+    else if (f.wr == 0) f.mode = fa2::kMaskCausal;
+  }
+  return f;
+}
+
+// The mask fields of the forward kernels' argument block.
+void set_mask_args(fa2::FwdArgs& args, const FoldedMask& f, const fa2_mask& m, int64_t H) {
+  args.wl = (int)f.wl;
+  args.wr = (int)f.wr;
+  args.prefix = (int)f.prefix;
+  args.H = (int)H;
+  args.seg = m.segment_ids;
+  // general masks whose tile cost grows with the query tile: heaviest first
+  args.grow = f.mode == fa2::kMaskGeneral && f.wl < 0 && f.wr >= 0;
+}
+
 // Query rows per workgroup of the kernel that serves head dim d.
 int64_t rows_per_workgroup(int64_t d) { return d == 256 ? fa2::w4::kBr : fa2::w8::kBr; }
 
@@ -385,10 +431,9 @@ int fa2_fwd_masked(const void* q, const void* k, const void* v, void* o, float* 
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
   const float c2 = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
-  fa2_mask m = {0, -1, -1, 0, nullptr};
-  if (mask) m = *mask;
-  if (m.window_left < -1 || m.window_right < -1 || m.prefix < 0) return FA2_ERR_MASK;
-  if (((uintptr_t)m.segment_ids) & 3) return FA2_ERR_MASK;
+  fa2_mask m;
+  const int mask_status = read_mask(mask, m);
+  if (mask_status != FA2_OK) return mask_status;
   if (B == 0 || H == 0 || N == 0) return FA2_OK;  // empty problem: nothing to do
   // Index limits: rows (plus the span of one pass of the segment-id scan) fit
   // in int32 inside the kernel, the grid in 2^31 - 1 workgroups, byte sizes in
@@ -415,23 +460,7 @@ int fa2_fwd_masked(const void* q, const void* k, const void* v, void* o, float* 
       return FA2_ERR_ALIAS;
   }
 
-  // ---- mask: fold the causal flag into the right bound, drop bounds that
-  // cannot bite, and pick the kernel's mask mode -----------------------------
-  int64_t wl = m.window_left, wr = m.window_right, prefix = m.prefix;
-  if (m.causal) wr = 0;  // key <= query, whatever right bound was given
-  if (wl >= N - 1) wl = -1;  // r - wl <= 0 for every row
-  if (wr >= N - 1) wr = -1;
-  if (prefix >= N) {  // every key is in the prefix: the window no longer matters
-    wl = -1;
-    wr = -1;
-    prefix = 0;
-  }
-  if (wl < 0 && wr < 0) prefix = 0;  // the window admits every key already
-  int mode = m.segment_ids ? fa2::kMaskSegments : fa2::kMaskGeneral;
-  if (!m.segment_ids && prefix == 0 && wl < 0) {
-    if (wr < 0) mode = fa2::kMaskNone;
-    else if (wr == 0) mode = fa2::kMaskCausal;
-  }
+  const FoldedMask f = fold_mask(m, N);
 
   // ---- device ---------------------------------------------------------------
   const int dev_status = check_device();
@@ -447,17 +476,12 @@ int fa2_fwd_masked(const void* q, const void* k, const void* v, void* o, float* 
   args.n_qtiles = (int)n_qtiles;
   args.n_wg = (int)(bh * n_qtiles);
   args.c2 = c2;
-  args.wl = (int)wl;
-  args.wr = (int)wr;
-  args.prefix = (int)prefix;
-  args.H = (int)H;
-  args.seg = m.segment_ids;
-  args.grow = mode == fa2::kMaskGeneral && wl < 0 && wr >= 0;
+  set_mask_args(args, f, m, H);
   args.descale_q = nullptr;
   args.descale_k = nullptr;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_d<0>(args, d, mode, s) : launch_d<1>(args, d, mode, s);
+  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_d<0>(args, d, f.mode, s) : launch_d<1>(args, d, f.mode, s);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FA2_ERR_LAUNCH;
@@ -481,10 +505,9 @@ int fa2_bwd_masked(const void* q, const void* k, const void* v, const void* o, c
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
   const float c2 = (float)((double)scale * 1.4426950408889634074);
   if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
-  fa2_mask m = {0, -1, -1, 0, nullptr};
-  if (mask) m = *mask;
-  if (m.window_left < -1 || m.window_right < -1 || m.prefix < 0) return FA2_ERR_MASK;
-  if (((uintptr_t)m.segment_ids) & 3) return FA2_ERR_MASK;
+  fa2_mask m;
+  const int mask_status = read_mask(mask, m);
+  if (mask_status != FA2_OK) return mask_status;
   if (B == 0 || H == 0 || N == 0) return FA2_OK;
   if (N > (int64_t)INT32_MAX - 65536) return FA2_ERR_SHAPE;
   if (B > INT32_MAX || H > INT32_MAX) return FA2_ERR_SHAPE;
@@ -512,23 +535,9 @@ int fa2_bwd_masked(const void* q, const void* k, const void* v, const void* o, c
     if (m.segment_ids && overlaps(out[i], out_n[i], m.segment_ids, (uint64_t)(B * N) * 4)) return FA2_ERR_ALIAS;
   }
 
-  // ---- mask: as in fa2_fwd_masked (the forward that produced lse must have
-  // used the same mask) --------------------------------------------------------
-  int64_t wl = m.window_left, wr = m.window_right, prefix = m.prefix;
-  if (m.causal) wr = 0;
-  if (wl >= N - 1) wl = -1;
-  if (wr >= N - 1) wr = -1;
-  if (prefix >= N) {
-    wl = -1;
-    wr = -1;
-    prefix = 0;
-  }
-  if (wl < 0 && wr < 0) prefix = 0;
-  int mode = m.segment_ids ? fa2::kMaskSegments : fa2::kMaskGeneral;
-  if (!m.segment_ids && prefix == 0 && wl < 0) {
-    if (wr < 0) mode = fa2::kMaskNone;
-    else if (wr == 0) mode = fa2::kMaskCausal;
-  }
+  // ---- mask: folded as in fa2_fwd_masked (the forward that produced lse must
+  // have used the same mask) ----------------------------------------------------
+  const FoldedMask f = fold_mask(m, N);
 
   // ---- device ---------------------------------------------------------------
   const int dev_status = check_device();
@@ -551,14 +560,15 @@ int fa2_bwd_masked(const void* q, const void* k, const void* v, const void* o, c
   args.n_q_wg = (int)n_q;
   args.scale = scale;
   args.c2 = c2;
-  args.wl = (int)wl;
-  args.wr = (int)wr;
-  args.prefix = (int)prefix;
+  args.wl = (int)f.wl;
+  args.wr = (int)f.wr;
+  args.prefix = (int)f.prefix;
   args.H = (int)H;
   args.seg = m.segment_ids;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_bwd_d<0>(args, d, mode, s) : launch_bwd_d<1>(args, d, mode, s);
+  hipError_t e =
+      dtype == FA2_DTYPE_FP16 ? launch_bwd_d<0>(args, d, f.mode, s) : launch_bwd_d<1>(args, d, f.mode, s);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FA2_ERR_LAUNCH;
@@ -592,9 +602,9 @@ int fa2_decode_static(const void* q, const void* k, const void* v, const int32_t
   return decode_entry(q, k, v, seqlens, o, lse, B, H, Mq, Nk, d, causal, scale, dtype, nullptr, 0, true, stream);
 }
 
-int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-                int64_t d, int causal, float scale, const float* descale_q, const float* descale_k, int dtype,
-                void* stream) {
+int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                       int64_t N, int64_t d, const fa2_mask* mask, float scale, const float* descale_q,
+                       const float* descale_k, int dtype, void* stream) {
   g_last_hip_error = 0;
   // ---- argument checks: no HIP call before they all pass -------------------
   if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
@@ -602,6 +612,9 @@ int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
   const float c2 = (float)((double)scale * 1.4426950408889634074);
   if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
+  fa2_mask m;
+  const int mask_status = read_mask(mask, m);
+  if (mask_status != FA2_OK) return mask_status;
   if (B == 0 || H == 0 || N == 0) return FA2_OK;
   if (N > (int64_t)INT32_MAX - 65536) return FA2_ERR_SHAPE;
   if (B > INT32_MAX || H > INT32_MAX) return FA2_ERR_SHAPE;
@@ -620,6 +633,12 @@ int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse
     if (overlaps(o, b16, in[j], in_n[j]) || overlaps(lse, lb, in[j], in_n[j])) return FA2_ERR_ALIAS;
   }
   if (overlaps(o, b16, lse, lb)) return FA2_ERR_ALIAS;
+  if (m.segment_ids) {
+    const uint64_t seg_bytes = (uint64_t)(B * N) * 4;
+    if (overlaps(m.segment_ids, seg_bytes, o, b16) || overlaps(m.segment_ids, seg_bytes, lse, lb))
+      return FA2_ERR_ALIAS;
+  }
+  const FoldedMask f = fold_mask(m, N);
 
   // ---- device ---------------------------------------------------------------
   const int dev_status = check_device();
@@ -635,26 +654,25 @@ int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse
   args.n_qtiles = (int)n_qtiles;
   args.n_wg = (int)(bh * n_qtiles);
   args.c2 = c2;
-  args.wl = -1;
-  args.wr = causal ? 0 : -1;
-  args.prefix = 0;
-  args.H = (int)H;
-  args.seg = nullptr;
-  args.grow = 0;
+  set_mask_args(args, f, m, H);
   args.descale_q = descale_q;
   args.descale_k = descale_k;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  if (dtype == FA2_DTYPE_FP16)
-    e = causal ? launch<fa2::kFp8Fp16, 128, fa2::kMaskCausal>(args, s) : launch<fa2::kFp8Fp16, 128, fa2::kMaskNone>(args, s);
-  else
-    e = causal ? launch<fa2::kFp8Bf16, 128, fa2::kMaskCausal>(args, s) : launch<fa2::kFp8Bf16, 128, fa2::kMaskNone>(args, s);
+  const hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_m<fa2::kFp8Fp16, 128>(args, f.mode, s)
+                                               : launch_m<fa2::kFp8Bf16, 128>(args, f.mode, s);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FA2_ERR_LAUNCH;
   }
   return FA2_OK;
+}
+
+int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+                int64_t d, int causal, float scale, const float* descale_q, const float* descale_k, int dtype,
+                void* stream) {
+  const fa2_mask m = {causal != 0, -1, -1, 0, nullptr};
+  return fa2_fwd_fp8_masked(q, k, v, o, lse, B, H, N, d, &m, scale, descale_q, descale_k, dtype, stream);
 }
 
 }  // extern "C"

@@ -277,6 +277,21 @@ int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse
                 int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                 const float* descale_q, const float* descale_k, int dtype, void* stream);
 
+/*
+ * fa2_fwd_fp8_masked -- fa2_fwd_fp8 under a general mask (NULL: no mask):
+ *
+ *   O = softmax(scale * q_real k_real^T + M) V,   L = log sum exp(...)
+ *
+ * with M the mask of fa2_fwd_masked (sliding window, prefix, segment ids; the
+ * mask as a 0 / -inf score term: "Flash Attention 2", section "Causal
+ * masking").  Arguments, layout, ownership and errors as for fa2_fwd_fp8, plus
+ * FA2_ERR_MASK (as for fa2_fwd_masked); segment_ids must not overlap o or lse.
+ * fa2_fwd_fp8(..., causal, ...) is this call with {causal, -1, -1, 0, NULL}.
+ */
+int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t N, int64_t d, const fa2_mask* mask, float scale,
+                       const float* descale_q, const float* descale_k, int dtype, void* stream);
+
 /* Bytes of workspace fa2_decode needs for these sizes (0: none), or minus a
  * fa2_status code for sizes fa2_decode would reject.  Host only; no HIP call. */
 int64_t fa2_decode_workspace_bytes(int64_t B, int64_t H, int64_t Mq, int64_t Nk, int64_t d);

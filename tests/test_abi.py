@@ -350,6 +350,42 @@ def test_fp8_valid_call_without_device_reports_device_error(lib):
     assert _fp8(dq=0, dk=0) == fa.FA2_ERR_DEVICE
 
 
+def _fp8_masked(mask, B=1, H=1, N=16, d=128, scale=0.125, dtype=0, o=O, lse=L, dq=DQS, dk=DKS):
+    return fa.fa2_fwd_fp8_masked(Q, K, V, o, lse, B, H, N, d, mask, scale, dq, dk, dtype, None)
+
+
+@pytest.mark.parametrize("fields,code", [
+    (dict(window_left=-2), fa.FA2_ERR_MASK), (dict(window_right=-5), fa.FA2_ERR_MASK),
+    (dict(prefix=-1), fa.FA2_ERR_MASK), (dict(segment_ids=0x60000002), fa.FA2_ERR_MASK),
+    (dict(segment_ids=O + 64), fa.FA2_ERR_ALIAS), (dict(segment_ids=L), fa.FA2_ERR_ALIAS),
+])
+def test_fp8_masked_argument_checks(lib, fields, code):
+    m = fa.Fa2Mask(0, -1, -1, 0, None)
+    for k_, v_ in fields.items():
+        setattr(m, k_, v_)
+    assert _fp8_masked(m) == code
+
+
+def test_fp8_masked_shared_checks(lib):
+    # the checks fa2_fwd_fp8 makes apply to the masked entry as well
+    m = fa.Fa2Mask(1, 4, 0, 2, None)
+    assert _fp8_masked(m, d=64) == fa.FA2_ERR_HEADDIM
+    assert _fp8_masked(m, dtype=2) == fa.FA2_ERR_DTYPE
+    assert _fp8_masked(m, o=Q) == fa.FA2_ERR_ALIAS
+    assert _fp8_masked(m, dq=DQS + 2) == fa.FA2_ERR_ALIGN
+    assert _fp8_masked(m, B=0) == fa.FA2_OK
+    assert _fp8_masked(None, N=0) == fa.FA2_OK
+
+
+def test_fp8_masked_valid_call_without_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    for mask in (None, fa.Fa2Mask(1, 5, 0, 3, 0xB0000000), fa.Fa2Mask(0, 7, 2, 0, None)):
+        for dtype in (0, 1):
+            assert _fp8_masked(mask, dtype=dtype, N=333) == fa.FA2_ERR_DEVICE
+
+
 def test_python_fp8_forward_rejects_bad_tensors(lib):
     import torch
     q8 = torch.zeros(1, 1, 8, 128, dtype=torch.float8_e4m3fn)

@@ -608,7 +608,7 @@ int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, flo
   g_last_hip_error = 0;
   // ---- argument checks: no HIP call before they all pass -------------------
   if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
-  if (d != 128) return FA2_ERR_HEADDIM;
+  if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
   const float c2 = (float)((double)scale * 1.4426950408889634074);
   if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
@@ -659,8 +659,13 @@ int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, flo
   args.descale_k = descale_k;
 
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = dtype == FA2_DTYPE_FP16 ? launch_m<fa2::kFp8Fp16, 128>(args, f.mode, s)
-                                               : launch_m<fa2::kFp8Bf16, 128>(args, f.mode, s);
+  hipError_t e;
+  if (d == 64)
+    e = dtype == FA2_DTYPE_FP16 ? launch_m<fa2::kFp8Fp16, 64>(args, f.mode, s)
+                                : launch_m<fa2::kFp8Bf16, 64>(args, f.mode, s);
+  else
+    e = dtype == FA2_DTYPE_FP16 ? launch_m<fa2::kFp8Fp16, 128>(args, f.mode, s)
+                                : launch_m<fa2::kFp8Bf16, 128>(args, f.mode, s);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FA2_ERR_LAUNCH;

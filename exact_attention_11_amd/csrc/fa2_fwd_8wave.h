@@ -106,14 +106,19 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   constexpr int DB = D / 32;                          // 32-wide output column blocks
   constexpr int kTile = kBc * D;                      // elements of one K, V or V^T slot
   constexpr int kLoads = kBc * CPR / (64 * kWaves);   // copy instructions per wave per V tile
-  constexpr int kLoadsK = kBc * CPRK / (64 * kWaves); // ... per K tile
+  // 1 KB copies per K tile.  With fewer than one per wave (e4m3 K at d = 64:
+  // 4 KB per tile) waves w and w + kKCopies copy the same rows (the same bytes
+  // to the same place), so every wave still issues one copy per tile and the
+  // copy counts the waits rely on stay uniform.
+  constexpr int kKCopies = kBc * CPRK / 64;
+  constexpr int kLoadsK = kKCopies < kWaves ? 1 : kKCopies / kWaves;  // ... per K tile
   constexpr int kRowStep = 4 * 16 * kWaves / CPR;     // rows covered by one instruction of all waves (V)
   constexpr int kRowStepK = 4 * 16 * kWaves / CPRK;   // ... (K)
   constexpr float kNegInf = -__builtin_huge_valf();
   static_assert(D == 64 || D == 128, "head dim");
-  static_assert(!kQK8 || D == 128, "fp8 instances serve head dim 128");
+  static_assert(kKCopies >= kWaves || kWaves % kKCopies == 0, "duplicated K copies");
   static_assert(kLoads >= 1 && kLoads * 64 * kWaves == kBc * CPR, "tile copy split");
-  static_assert(kLoadsK >= 1 && kLoadsK * 64 * kWaves == kBc * CPRK, "tile copy split");
+  static_assert(kLoadsK >= 1 && (kKCopies < kWaves || kLoadsK * 64 * kWaves == kBc * CPRK), "tile copy split");
   // Copy instructions per wave per tile: K and V, plus the keys' segment ids
   // under segment ids (issued by every wave, so the counts stay uniform).
   constexpr int kTileLoads = kLoadsK + kLoads + (kSeg ? 1 : 0);
@@ -161,8 +166,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
   const uint32_t voffV = (uint32_t)((vr * D + cch * 8) * 2);
   // The same for K with its own row length (CPRK chunks); LDS row krK holds
   // key sigma(krK).
-  const int cchK = (4 * wave) % CPRK + (lane >> 4);
-  const int krK = 16 * ((4 * wave) / CPRK) + (lane & 15);
+  const int wk = kKCopies < kWaves ? wave % kKCopies : wave;  // this wave's K copy slot
+  const int cchK = (4 * wk) % CPRK + (lane >> 4);
+  const int krK = 16 * ((4 * wk) / CPRK) + (lane & 15);
   const uint32_t voffK = (uint32_t)(sigma(krK) * D * kEbK + cchK * 16);
 
   // Key tiles: step st of the loop visits tile tile_of(st), st < nt.  Without a
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_8wave(FwdArgs a) {
     }
     const int t = p - (kSeg ? 1 : 0);
     if (t < kLoadsK) {
-      FA2_LDS uint16_t* dk = sK + slot * kTile + (t * kWaves + wave) * 64 * 8;
+      FA2_LDS uint16_t* dk = sK + slot * kTile + (t * kWaves + wk) * 64 * 8;
       if (kv0 + kBc <= N) {
         dma16_sbase(kh + (int64_t)kv0 * D * kEbK + t * kRowStepK * D * kEbK, voffK, dk);
       } else {

@@ -520,8 +520,8 @@ def main() -> int:
     else:
         mask_kw = {}
     if args.fp8:
-        if w.d not in (64, 128):
-            log("the fp8 forward pass serves head dims 64 and 128")
+        if w.d not in (64, 128, 256):
+            log("the fp8 forward pass serves head dims 64, 128 and 256")
             return 2
         from exact_attention_11_amd.inputs import make_qkv_fp8
         q8, k8, v16, dsq, dsk = make_qkv_fp8(w.B, w.H, w.N, w.d, q.dtype, w.dist, seed=0)

@@ -608,7 +608,7 @@ int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, flo
   g_last_hip_error = 0;
   // ---- argument checks: no HIP call before they all pass -------------------
   if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
+  if (d != 64 && d != 128 && d != 256) return FA2_ERR_HEADDIM;
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_DTYPE;
   const float c2 = (float)((double)scale * 1.4426950408889634074);
   if (!std::isfinite(scale) || !std::isfinite(c2)) return FA2_ERR_SCALE;
@@ -619,7 +619,8 @@ int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, flo
   if (N > (int64_t)INT32_MAX - 65536) return FA2_ERR_SHAPE;
   if (B > INT32_MAX || H > INT32_MAX) return FA2_ERR_SHAPE;
   const int64_t bh = B * H;
-  const int64_t n_qtiles = (N + fa2::w8::kBr - 1) / fa2::w8::kBr;
+  const int64_t br = rows_per_workgroup(d);
+  const int64_t n_qtiles = (N + br - 1) / br;
   if (bh > (int64_t)INT32_MAX / n_qtiles) return FA2_ERR_SHAPE;
   if (bh > (INT64_MAX / 4) / (N * d)) return FA2_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULLPTR;
@@ -639,6 +640,8 @@ int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, flo
       return FA2_ERR_ALIAS;
   }
   const FoldedMask f = fold_mask(m, N);
+  // Head dim 256 in fp8 runs on the pair kernel: no mask or the causal mask.
+  if (d == 256 && f.mode != fa2::kMaskNone && f.mode != fa2::kMaskCausal) return FA2_ERR_MASK;
 
   // ---- device ---------------------------------------------------------------
   const int dev_status = check_device();
@@ -660,12 +663,19 @@ int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, flo
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (d == 64)
+  if (d == 64) {
     e = dtype == FA2_DTYPE_FP16 ? launch_m<fa2::kFp8Fp16, 64>(args, f.mode, s)
                                 : launch_m<fa2::kFp8Bf16, 64>(args, f.mode, s);
-  else
+  } else if (d == 128) {
     e = dtype == FA2_DTYPE_FP16 ? launch_m<fa2::kFp8Fp16, 128>(args, f.mode, s)
                                 : launch_m<fa2::kFp8Bf16, 128>(args, f.mode, s);
+  } else if (f.mode == fa2::kMaskCausal) {
+    e = dtype == FA2_DTYPE_FP16 ? launch<fa2::kFp8Fp16, 256, fa2::kMaskCausal>(args, s)
+                                : launch<fa2::kFp8Bf16, 256, fa2::kMaskCausal>(args, s);
+  } else {
+    e = dtype == FA2_DTYPE_FP16 ? launch<fa2::kFp8Fp16, 256, fa2::kMaskNone>(args, s)
+                                : launch<fa2::kFp8Bf16, 256, fa2::kMaskNone>(args, s);
+  }
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FA2_ERR_LAUNCH;

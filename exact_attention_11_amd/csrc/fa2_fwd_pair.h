@@ -72,11 +72,19 @@ template <int kDType, int kMask>
 __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   constexpr bool kCausal = kMask == kMaskCausal;
   static_assert(kMask == kMaskNone || kMask == kMaskCausal, "no mask or the causal mask");
-  typedef Elem<kDType> E;
+  // fp8 instances: S = K Q^T on the fp8 MFMA from e4m3 Q and K (one byte per
+  // element); V, P and O stay 16-bit.
+  constexpr bool kQK8 = kDType == kFp8Fp16 || kDType == kFp8Bf16;
+  typedef Elem<kDType & 1> E;
   typedef typename E::V8 V8;
-  constexpr int KS = D / 16;  // k-steps of S
+  typedef std::conditional_t<kQK8, i32x8, V8> QF;  // one S operand fragment of Q
+  constexpr int kEbK = kQK8 ? 1 : 2;                 // bytes per element of Q and K
+  constexpr int CPRK = D * kEbK / 16;                 // 16-byte chunks per K row
+  constexpr int KS = kQK8 ? D / 64 : D / 16;          // k-steps of S
   constexpr int DBH = 4;      // 32-column output blocks per wavefront (half the head dim)
-  constexpr int kNs = KS;     // S fragments
+  // S fragments: one per 16-bit MFMA; an fp8 operand is two 16-byte halves,
+  // loaded as consecutive fragments 2 ks and 2 ks + 1.
+  constexpr int kNs = kQK8 ? 2 * KS : KS;
   constexpr int kNpv = 4 * DBH;  // P.V fragments: 4 key steps x 4 output blocks
   constexpr int kPipe = 4;
   constexpr float kNegInf = -__builtin_huge_valf();
@@ -107,9 +115,15 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   const int q_row0 = qtile * kBr + (wave >> 1) * 32;
   const int my_q = q_row0 + col;
   const int64_t head_off = (int64_t)bh * N * D;
-  const uint16_t* __restrict__ kh_ptr = a.k + head_off;
+  const uint16_t* __restrict__ kh_ptr = a.k + head_off;             // K of this head (16-bit instances)
+  const char* __restrict__ kh_b = (const char*)a.k + head_off * kEbK;  // the same, bytes (e4m3 instances)
   const uint16_t* __restrict__ vh_ptr = a.v + head_off;
-  const float c2 = a.c2;
+  // Score multiplier in log2 units (the fp8 instances fold in the descales).
+  float c2 = a.c2;
+  if constexpr (kQK8) {
+    if (a.descale_q) c2 *= a.descale_q[bh];
+    if (a.descale_k) c2 *= a.descale_k[bh];
+  }
   const bool pos = c2 > 0.f;  // -inf times the multiplier stays -inf: mask raw scores
   // A pair whose 32 rows all lie past N (the last query tile of a ragged N)
   // skips its products and softmax and only issues its share of the copies.
@@ -125,18 +139,23 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   // st as its softmax phase opens (vector work only), group 0 the K tile st + 1
   // between its P.V products (one copy every second MFMA), which still leaves
   // a phase and a half for the copies to land before the next step.
-  // Copy-wave c = wave % 4, instruction t (0..7) fills 1 KB:
-  //  * K: blocks 4 (4t + c) .. + 3, i.e. rows 16 (t / 2) + lane % 16 of chunk
-  //    16 (t % 2) + 4c + lane / 16: one lane offset, the rest in the scalar base;
+  // Copy-wave c = wave % 4, instruction t fills 1 KB:
+  //  * K (kTPR = CPRK / 16 instructions per 16 rows: 2 for 16-bit K, 1 for
+  //    e4m3): blocks 4 (4t + c) .. + 3, i.e. rows 16 (t / kTPR) + lane % 16 of
+  //    chunk 16 (t % kTPR) + 4c + lane / 16: one lane offset, the rest in the
+  //    scalar base;
   //  * V: 16-byte slots 64 (4t + c) + lane, i.e. row 8t + 2c + lane / 32, stored
   //    chunk lane % 32 holding logical chunk (lane % 32) ^ swz_v(row) (row % 4
   //    does not depend on t).
   constexpr int kCopyWaves = 4;
-  constexpr int kLoads = kBc * CPR / (64 * kCopyWaves);  // copy instructions per copy-wave per tile (8)
+  constexpr int kLoads = kBc * CPR / (64 * kCopyWaves);    // V copy instructions per copy-wave per tile (8)
+  constexpr int kLoadsK = kBc * CPRK / (64 * kCopyWaves);  // K: 8, or 4 for e4m3
+  constexpr int kTPR = CPRK / 16;
   static_assert(kLoads * 64 * kCopyWaves == kBc * CPR, "tile copy split");
+  static_assert(kLoadsK * 64 * kCopyWaves == kBc * CPRK && kTPR >= 1, "K tile copy split");
   const int cw = wave & 3;
   const int krow = lane & 15, kch = 4 * cw + (lane >> 4);
-  const uint32_t voffK = (uint32_t)((krow * D + kch * 8) * 2);
+  const uint32_t voffK = kQK8 ? (uint32_t)(krow * D + kch * 16) : (uint32_t)((krow * D + kch * 8) * 2);
   const int vrow = 2 * cw + (lane >> 5);
   const int vch = (lane & 31) ^ swz_v(vrow);
   const uint32_t voffV = (uint32_t)((vrow * D + vch * 8) * 2);
@@ -144,7 +163,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   auto issue_k1 = [&](int tile, int slot, int t) __attribute__((always_inline)) {
     const int kv0 = tile * kBc;
     FA2_LDS uint16_t* dk = sK + slot * kTile + (t * kCopyWaves + cw) * 512;
-    if (kv0 + kBc <= N) {
+    if constexpr (kQK8) {
+      if (kv0 + kBc <= N) {
+        dma16_sbase(kh_b + (int64_t)kv0 * D + t * 16 * D, voffK, dk);
+      } else {
+        const int g = min(kv0 + t * 16 + krow, N - 1);
+        dma16(kh_b + (int64_t)g * D + kch * 16, dk);
+      }
+    } else if (kv0 + kBc <= N) {
       dma16_sbase((const char*)(kh_ptr + (int64_t)kv0 * D) + (t >> 1) * 16 * D * 2 + (t & 1) * 256, voffK, dk);
     } else {
       // Ragged last tile: rows past N re-read row N-1 (their scores are masked).
@@ -154,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   };
   auto issue_k = [&](int tile, int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < kLoads; ++t) issue_k1(tile, slot, t);
+    for (int t = 0; t < kLoadsK; ++t) issue_k1(tile, slot, t);
   };
   auto issue_v = [&](int tile, int slot) __attribute__((always_inline)) {
     const int kv0 = tile * kBc;
@@ -189,8 +215,19 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   // Q fragments (B operand of S^T = K Q^T) over the whole head dim, kept in
   // registers; consumed here so that the compiler's wait for them (which also
   // covers the copy above) stays out of the loop.
-  V8 qf[KS];
-  {
+  QF qf[KS];
+  if constexpr (kQK8) {
+    // Lane (hl, col): bytes 64 ks + 32 hl .. + 31 of its query row.
+    const char* qp = (const char*)a.q + head_off + (int64_t)min(my_q, N - 1) * D + 32 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 lo = *(const u32x4*)(qp + 64 * ks);
+      const u32x4 hi = *(const u32x4*)(qp + 64 * ks + 16);
+      // (two 128-bit operands: a 256-bit "v" operand is invalid for the host pass)
+      asm volatile("" ::"v"(lo), "v"(hi));
+      qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  } else {
     const uint16_t* qp = a.q + head_off + (int64_t)min(my_q, N - 1) * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(qp + 16 * ks));
@@ -207,7 +244,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   float mx = kNegInf;     // their row max (raw units when pos, else log2 units)
   uint32_t pk[8];         // packed weights of this wavefront's 32 keys, B-operand order
 
-  // Operand addresses.  K: lane (hl, col) reads key 32 kh + col, chunk 2 ks + hl.
+  // Operand addresses.  K: lane (hl, col) reads key 32 kh + col, chunk 2 ks + hl
+  // (e4m3: chunks 4 ks + 2 hl and + 1).
   // V^T (output block 4 kh + j, key step c of 16 keys): lane (g, L) = (lane / 16,
   // lane % 16) takes keys 16 c + 4 (g / 2) + L / 4 and + 8 of columns 32 (4 kh + j)
   // + 16 (g % 2) + 4 (L % 4) .. + 3, i.e. the key order the score registers hold
@@ -215,7 +253,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   // two key steps of this wavefront's own half first (weights in registers),
   // then the partner's two (weights from LDS): one base address per (half, j),
   // everything else an immediate.
-  const uint32_t kaddr0 = (uint32_t)(((((2 * kh + (col >> 4)) * CPR) + hl) << 8) + ((col & 15) << 4));
+  const uint32_t kaddr0 =
+      (uint32_t)(((((2 * kh + (col >> 4)) * CPRK) + (kQK8 ? 2 * hl : hl)) << 8) + ((col & 15) << 4));
   uint32_t vaddr0[2][4];
   {
     const int g = lane >> 4, L = lane & 15;
@@ -237,7 +276,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   // j = f % 4.
   auto load_op = [&](uint32_t kbase, const uint32_t (*vb)[4], int i) __attribute__((always_inline)) {
     if (i < kNs) {
-      return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(size_t)(kbase + (uint32_t)((2 * i) << 8)));
+      const int chunk = kQK8 ? 4 * (i >> 1) + (i & 1) : 2 * i;
+      return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(size_t)(kbase + (uint32_t)(chunk << 8)));
     }
     const int f = i - kNs, cp = f >> 2, j = f & 3;
     const uint32_t ad = vb[cp >> 1][j] + (uint32_t)(16 * (cp & 1) * CPR * 16);
@@ -255,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   // for the loop: on the first step the weights are all zero and the V slot
   // holds zeros, and the closing step's scores are not used.
   // kCopyK (compile-time, group 0): also issue the copies of K tile st + 1,
-  // one after every second P.V product.
+  // one after every second P.V product (every fourth for e4m3 K).
   auto products = [&](int st, auto kCopyK) __attribute__((always_inline)) {
     constexpr bool copy_k = decltype(kCopyK)::value;
     const bool k_next = st + 1 < nt;
@@ -271,11 +311,25 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < kPipe; ++i) fr[i] = load_op(kbase, vb, i);
     uint32_t pp[8];
+    constexpr int kCopyStride = kNpv / kLoadsK;
 #pragma unroll
     for (int i = 0; i < kNs + kNpv; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       if (i < kNs) {
-        sa = E::mfma(fr[i % kPipe], qf[i], sa);
+        if constexpr (kQK8) {
+          // An fp8 MFMA takes the fragment pair (i - 1, i): issue it on the
+          // second half, and reload the pair's slots only then.
+          if (i & 1) {
+            const u32x4 lo = __builtin_bit_cast(u32x4, fr[(i - 1) % kPipe]);
+            const u32x4 hi = __builtin_bit_cast(u32x4, fr[i % kPipe]);
+            const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            sa = mfma_fp8(ka, qf[i >> 1], sa);
+            if (i - 1 + kPipe < kNs + kNpv) fr[(i - 1) % kPipe] = load_op(kbase, vb, i - 1 + kPipe);
+          }
+        } else {
+          sa = E::mfma(fr[i % kPipe], qf[i], sa);
+        }
       } else {
         const int f = i - kNs, cp = f >> 2, j = f & 3;
         if (f == 8) {  // the partner's weights, needed from here on
@@ -291,8 +345,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
         const u32x4 bw = {w[4 * (cp & 1) + 0], w[4 * (cp & 1) + 1], w[4 * (cp & 1) + 2], w[4 * (cp & 1) + 3]};
         o[j] = E::mfma(fr[i % kPipe], __builtin_bit_cast(V8, bw), o[j]);
       }
-      if (i + kPipe < kNs + kNpv) fr[i % kPipe] = load_op(kbase, vb, i + kPipe);
-      if (copy_k && i >= kNs && ((i - kNs) & 1) == 0 && k_next) issue_k1(st + 1, (st + 1) & 1, (i - kNs) >> 1);
+      if (i + kPipe < kNs + kNpv && !(kQK8 && i < kNs && (i & 1) == 0)) fr[i % kPipe] = load_op(kbase, vb, i + kPipe);
+      if (copy_k && i >= kNs && ((i - kNs) % kCopyStride) == 0 && k_next)
+        issue_k1(st + 1, (st + 1) & 1, (i - kNs) / kCopyStride);
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);

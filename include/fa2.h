@@ -272,7 +272,7 @@ int fa2_decode_static(const void* q, const void* k, const void* v, const int32_t
  * descale_q, descale_k : [B*H] float32 device arrays (read only, 4-byte
  *              aligned), or NULL for all ones.
  * Other arguments, layout rules, errors and the empty-problem rule as for
- * fa2_fwd; d must be 64 or 128 (FA2_ERR_HEADDIM otherwise).
+ * fa2_fwd; d must be 64, 128 or 256 (FA2_ERR_HEADDIM otherwise).
  */
 int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                 int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
@@ -286,7 +286,8 @@ int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse
  * with M the mask of fa2_fwd_masked (sliding window, prefix, segment ids; the
  * mask as a 0 / -inf score term: "Flash Attention 2", section "Causal
  * masking").  Arguments, layout, ownership and errors as for fa2_fwd_fp8, plus
- * FA2_ERR_MASK (as for fa2_fwd_masked); segment_ids must not overlap o or lse.
+ * FA2_ERR_MASK (as for fa2_fwd_masked, and for a mask other than none or
+ * causal at d = 256); segment_ids must not overlap o or lse.
  * fa2_fwd_fp8(..., causal, ...) is this call with {causal, -1, -1, 0, NULL}.
  */
 int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -324,7 +324,7 @@ def _fp8(B=1, H=1, N=16, d=128, causal=0, scale=0.125, dtype=0, q=Q, k=K, v=V, o
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(B=-1), fa.FA2_ERR_SHAPE), (dict(N=2 ** 31), fa.FA2_ERR_SHAPE),
-    (dict(d=32), fa.FA2_ERR_HEADDIM), (dict(d=256), fa.FA2_ERR_HEADDIM),
+    (dict(d=32), fa.FA2_ERR_HEADDIM), (dict(d=192), fa.FA2_ERR_HEADDIM),
     (dict(dtype=2), fa.FA2_ERR_DTYPE), (dict(scale=math.inf), fa.FA2_ERR_SCALE),
     (dict(q=0), fa.FA2_ERR_NULLPTR), (dict(v=0), fa.FA2_ERR_NULLPTR), (dict(lse=0), fa.FA2_ERR_NULLPTR),
     (dict(k=K + 8), fa.FA2_ERR_ALIGN), (dict(dq=DQS + 2), fa.FA2_ERR_ALIGN),
@@ -346,7 +346,7 @@ def test_fp8_valid_call_without_device_reports_device_error(lib):
         pytest.skip("a GPU is present: this call would launch on fake pointers")
     for dtype in (0, 1):
         for causal in (0, 1):
-            for d in (64, 128):
+            for d in (64, 128, 256):
                 assert _fp8(dtype=dtype, causal=causal, N=4099, d=d) == fa.FA2_ERR_DEVICE
     assert _fp8(dq=0, dk=0) == fa.FA2_ERR_DEVICE
 
@@ -370,7 +370,10 @@ def test_fp8_masked_argument_checks(lib, fields, code):
 def test_fp8_masked_shared_checks(lib):
     # the checks fa2_fwd_fp8 makes apply to the masked entry as well
     m = fa.Fa2Mask(1, 4, 0, 2, None)
-    assert _fp8_masked(m, d=256) == fa.FA2_ERR_HEADDIM
+    assert _fp8_masked(m, d=512) == fa.FA2_ERR_HEADDIM
+    # head dim 256 in fp8: no mask or the causal mask only
+    assert _fp8_masked(m, d=256) == fa.FA2_ERR_MASK
+    assert _fp8_masked(fa.Fa2Mask(0, -1, -1, 0, 0xB0000000), d=256) == fa.FA2_ERR_MASK
     assert _fp8_masked(m, dtype=2) == fa.FA2_ERR_DTYPE
     assert _fp8_masked(m, o=Q) == fa.FA2_ERR_ALIAS
     assert _fp8_masked(m, dq=DQS + 2) == fa.FA2_ERR_ALIGN
@@ -385,6 +388,9 @@ def test_fp8_masked_valid_call_without_device_reports_device_error(lib):
     for mask in (None, fa.Fa2Mask(1, 5, 0, 3, 0xB0000000), fa.Fa2Mask(0, 7, 2, 0, None)):
         for dtype in (0, 1):
             assert _fp8_masked(mask, dtype=dtype, N=333) == fa.FA2_ERR_DEVICE
+    # masks that reduce to none or causal are accepted at head dim 256
+    for mask in (fa.Fa2Mask(1, -1, -1, 0, None), fa.Fa2Mask(0, 400, 400, 0, None), fa.Fa2Mask(0, -1, 0, 0, None)):
+        assert _fp8_masked(mask, d=256, N=333) == fa.FA2_ERR_DEVICE
 
 
 def test_python_fp8_forward_rejects_bad_tensors(lib):

@@ -1,15 +1,17 @@
 """GPU parity of the fp8 forward pass (fa2_fwd_fp8 and fa2_fwd_fp8_masked
 through the C ABI: Q and K in OCP e4m3 with per-head descales, V and O in
-fp16/bf16, head dims 64 and 128) against the fp64 oracles (oracle/attention_ref.c,
+fp16/bf16, head dims 64, 128 and 256) against the fp64 oracles (oracle/attention_ref.c,
 oracle/attention_mask_ref.c) run on the real inputs q8 * descale_q,
 k8 * descale_k and V.
 
 The fp8 MFMA (v_mfma_f32_32x32x64_f8f6f4) sums the 64 products of one
-instruction with an error of up to about 2^-11 of the largest of them
-(test_fp8_score_accumulation_bound pins 2^-10 on many dot products), so a score
-s_rc carries an error |delta_rc| <= eps_rc = 2^-10 * |scale| * descale_q *
-descale_k * max_k |q8_rk k8_ck|; the weights and P.V are those of the 16-bit
-forward pass.  The tolerances are the 16-bit ones by V's type (max |dO| <= 2e-3
+instruction with an error of up to about 2^-11 of the largest of them, and a
+score adds the d / 64 instructions' results in fp32
+(test_fp8_score_accumulation_bound pins 2^-10 per instruction on many dot
+products), so a score s_rc carries an error |delta_rc| <= eps_rc = 2^-10 *
+|scale| * descale_q * descale_k * sum over the 64-element groups g of
+max_{k in g} |q8_rk k8_ck|; the weights and P.V are those of the 16-bit forward
+pass.  The tolerances are the 16-bit ones by V's type (max |dO| <= 2e-3
 for fp16, 1e-2 for bf16; max |dL| <= 1e-3) plus, per row r, what the score
 errors can do, with E_r = sum_c p_rc eps_rc and e_r = max_c eps_rc over the
 visible keys (p from the fp64 scores): since log sum_c p_c exp(delta_c) lies
@@ -49,13 +51,14 @@ def _real(x8, ds, B, H):
     return (x8.to(torch.float64) * ds.to(torch.float64).reshape(B, H, 1, 1)).numpy()
 
 
-ACC_REL = 2.0 ** -10  # score error per unit of the largest product (pinned below)
+ACC_REL = 2.0 ** -10  # score error per instruction, per unit of its largest product (pinned below)
 
 
 def _score_error_terms(q8, k8, dq, dk, scale, l_ref, allowed=None, rows=None):
     """Per row of each (b, h): E_r = sum_c p_rc eps_rc and e_r = max_c eps_rc
     over the visible keys, eps_rc = ACC_REL |scale| descale_q descale_k
-    max_k |q8_rk k8_ck| and p_rc = exp(s_rc - L_r) from the fp64 scores and the
+    sum_g max_{k in g} |q8_rk k8_ck| (g: the 64-element groups of one MFMA) and
+    p_rc = exp(s_rc - L_r) from the fp64 scores and the
     oracle's L.  allowed: [B or 1, N, N] booleans, "causal" (key <= row), or
     None (every key)."""
     B, H, N, d = q8.shape
@@ -70,8 +73,11 @@ def _score_error_terms(q8, k8, dq, dk, scale, l_ref, allowed=None, rows=None):
         for h in range(H):
             a, c = np.abs(qs[b, h][rows]), np.abs(ks[b, h])
             m = np.zeros((len(rows), N))
-            for u in range(d):
-                np.maximum(m, np.outer(a[:, u], c[:, u]), out=m)
+            for g0 in range(0, d, 64):
+                mg = np.zeros((len(rows), N))
+                for u in range(g0, g0 + 64):
+                    np.maximum(mg, np.outer(a[:, u], c[:, u]), out=mg)
+                m += mg
             eps = ACC_REL * abs(scale) * dqs[b, h] * dks[b, h] * m
             s = scale * dqs[b, h] * dks[b, h] * (qs[b, h][rows] @ ks[b, h].T)
             p = np.exp(np.minimum(s - l_ref[b, h][rows][:, None], 0.0))
@@ -117,24 +123,63 @@ def _case(B, H, N, v_dtype, causal, dist="normal", seed=0, descales=True, scale=
     _check(what, o, lse, o_ref, l_ref, v_dtype, E, emax, float(v.double().abs().max()))
 
 
-@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 255, 256, 257, 600, 1000])
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 600, 1000])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("v_dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fp8_parity_ragged_sweep(d, v_dtype, causal, N):
     _case(1, 2, N, v_dtype, causal, seed=1, d=d)
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fp8_parity_batch_heads(d, causal):
     _case(2, 3, 700, torch.float16, causal, seed=2, d=d)
 
 
-def test_fp8_parity_head_dim_64_peaky_and_unusual_scales():
-    _case(1, 2, 900, torch.bfloat16, False, dist="peaky", seed=4, d=64)
-    _case(1, 2, 300, torch.float16, True, seed=5, scale=0.0, d=64)
-    _case(1, 2, 300, torch.float16, True, seed=5, scale=-0.05, d=64)
+@pytest.mark.parametrize("d", [64, 256])
+def test_fp8_parity_other_head_dims_peaky_and_unusual_scales(d):
+    _case(1, 2, 900, torch.bfloat16, False, dist="peaky", seed=4, d=d)
+    _case(1, 2, 300, torch.float16, True, seed=5, scale=0.0, d=d)
+    _case(1, 2, 300, torch.float16, True, seed=5, scale=-0.05, d=d)
+
+
+def test_fp8_head_dim_256_full_size_sampled():
+    """The head-dim-256 workload's shape (4 x 8 heads x 4099 rows, ragged) in
+    fp8, no mask: every head against the oracle on strided rows."""
+    B, H, N, d = 4, 8, 4099, 256
+    q8, k8, v, dq, dk = make_qkv_fp8(B, H, N, d, torch.bfloat16, "normal", 9)
+    _log(f"case fp8 full size B={B} H={H} N={N} d={d}")
+    o, lse = fa.forward_fp8(q8.cuda(), k8.cuda(), v.cuda(), dq.cuda(), dk.cuda())
+    torch.cuda.synchronize()
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    rows = np.concatenate([np.arange(0, 130), np.arange(130, N - 130, 211), np.arange(N - 130, N)]).astype(np.int64)
+    vmax = float(v.double().abs().max())
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            bh = b * H + h
+            qq = (q8[b, h].to(torch.float64) * float(dq[bh])).numpy()
+            kk = (k8[b, h].to(torch.float64) * float(dk[bh])).numpy()
+            o_ref, l_ref = oracle.attention_rows_f64(qq, kk, v[b, h].double().numpy(), rows, False, scale)
+            lfull = np.zeros((1, 1, N))
+            lfull[0, 0, rows] = l_ref
+            E, emax = _score_error_terms(q8[b:b + 1, h:h + 1], k8[b:b + 1, h:h + 1], dq[bh:bh + 1], dk[bh:bh + 1],
+                                         scale, lfull, None, rows)
+            E, emax = E[0, 0], emax[0, 0]
+            do = np.abs(o[b, h].cpu().double().numpy()[rows] - o_ref).max(axis=-1)
+            dl = np.abs(lse[b, h].cpu().double().numpy()[rows] - l_ref)
+            worst = max(worst, float(do.max()))
+            assert np.all(do <= TOL_O[torch.bfloat16] + vmax * (2.0 * E + emax ** 2) * np.exp(2.0 * emax)), (b, h)
+            assert np.all(dl <= TOL_L + E + emax ** 2), (b, h, dl.max())
+    _log(f"  worst max|dO| over {B * H} heads: {worst:.3e}")
+
+
+def test_fp8_head_dim_256_rejects_general_masks():
+    q8, k8, v, dq, dk = make_qkv_fp8(1, 2, 100, 256, torch.float16, "normal", 1)
+    with pytest.raises(fa.Fa2Error) as e:
+        fa.forward_fp8(q8.cuda(), k8.cuda(), v.cuda(), window=(10, 0))
+    assert e.value.status == fa.FA2_ERR_MASK
 
 
 def test_fp8_parity_without_descales_and_peaky():
@@ -266,13 +311,14 @@ def test_fp8_masked_reductions_match_plain_entry(d):
 
 
 @pytest.mark.parametrize("kind", ["normal", "peaky", "mixed_exponents"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fp8_score_accumulation_bound(d, kind):
     """With one key L equals the score, so many heads of N = 1 measure the fp8
-    MFMA's dot products one by one: |L - q.k| <= 2^-10 max_k |q_k k_k| (plus the
-    fp32 rounding of L), the bound the tolerances above rest on.  Mixed
-    exponents (products spread over 2^-12 .. 2^14) come closest (about 2^-11.1
-    measured); products of one size are almost exact."""
+    MFMA's dot products one by one: |L - q.k| <= 2^-10 sum_g max_{k in g}
+    |q_k k_k| over the 64-element groups of one instruction (plus the fp32
+    rounding of L), the bound the tolerances above rest on.  Mixed exponents
+    (products spread over 2^-12 .. 2^14) come closest (about 2^-11.3 of the
+    largest product at d = 64); products of one size are almost exact."""
     H = 4096
     rng = np.random.default_rng({"normal": 1, "peaky": 2, "mixed_exponents": 3}[kind] + d)
     if kind == "normal":
@@ -291,6 +337,7 @@ def test_fp8_score_accumulation_bound(d, kind):
     prod = q8.to(torch.float64).numpy() * k8.to(torch.float64).numpy()
     exact = prod.sum(-1)[..., 0]
     err = np.abs(lse.cpu().double().numpy()[..., 0] - exact)
-    bound = ACC_REL * np.abs(prod).max(-1)[..., 0] + 2.0 ** -22 * np.abs(exact)
-    _log(f"case d={d} {kind}: max err / largest product = 2^{np.log2(max((err / np.abs(prod).max(-1)[..., 0]).max(), 1e-30)):.1f}")
+    gmax = np.abs(prod).reshape(prod.shape[:-1] + (d // 64, 64)).max(-1).sum(-1)[..., 0]
+    bound = ACC_REL * gmax + 2.0 ** -22 * np.abs(exact)
+    _log(f"case d={d} {kind}: max err / sum of group maxima = 2^{np.log2(max((err / gmax).max(), 1e-30)):.1f}")
     assert np.all(err <= bound), (kind, float((err / bound).max()))

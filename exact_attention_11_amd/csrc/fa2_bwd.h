@@ -298,8 +298,14 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
   if constexpr (kVLds) load_rows<D, kKeysPerWg, kGeneral>(a.v + head_off, sV, kt * kKeysPerWg, N, wave, lane);
   load_tile(it0, 0);
 
-  // The segment id of this lane's key.
+  // The segment id of this lane's key; whether the wave's 32 keys share one id.
   const int seg_k = kSeg ? segb[min(my_k, N - 1)] : 0;
+  int seg_w = 0;
+  bool keys_one_seg = false;
+  if constexpr (kSeg) {
+    seg_w = wave_min(seg_k);
+    keys_one_seg = seg_w == wave_max(seg_k);
+  }
   // K and V of this lane's key (B operands of S = Q K^T and dP = dO V^T).
   V8 kf[KS], vf[kVLds ? 1 : KS];
   {
@@ -381,7 +387,18 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
       }
       // Element e of the accumulators is query q0 + 8*(e/4) + 4*hl + e%4 of this
       // lane's key; its L and D sit at the same offset in the stat rows.
-      const bool need_mask = kGeneral || (q0 + 32 > N) || (kCausal && kw0 + 31 > q0);
+      bool need_mask = (q0 + 32 > N) || (kCausal && kw0 + 31 > q0);
+      if constexpr (kGeneral) {
+        // (wave-uniform) every pair of the 32 x 32 block visible: all rows and
+        // keys below N, the keys all in the prefix or the window satisfied at
+        // the block's corners, and under segment ids one id for all of them.
+        bool full = q0 + 31 < N && kw0 + 31 < N &&
+                    (kw0 + 31 < a.prefix || ((a.wl < 0 || kw0 >= q0 + 31 - a.wl) && (a.wr < 0 || kw0 + 31 <= q0 + a.wr)));
+        if constexpr (kSeg) {
+          if (full) full = keys_one_seg && __all(tG[sb * 32 + col] == seg_w);
+        }
+        need_mask = !full;
+      }
       const int lim_n = N - q0 - 4 * hl;          // query < N      <=> qi < lim_n
       const int lim_c = my_k - q0 - 4 * hl;       // key <= query   <=> qi >= lim_c
       uint32_t pp[2][4], pd[2][4];                // P and dS packed, per 16-query k-step
@@ -566,6 +583,12 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
   const float l2 = a.lse[(int64_t)bh * N + rq] * kLog2e;
   const float dd = a.delta[(int64_t)bh * N + rq];
   const int seg_q = kSeg ? segb[rq] : 0;
+  int seg_w = 0;
+  bool rows_one_seg = false;  // the wave's 32 rows share one segment id
+  if constexpr (kSeg) {
+    seg_w = wave_min(seg_q);
+    rows_one_seg = seg_w == wave_max(seg_q);
+  }
 
   f32x16 dqt[DB];  // dQ^T: rows = head dim, columns = this wave's queries
 #pragma unroll
@@ -602,9 +625,21 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
       }
     }
     // Element (kb, e) is key kv0 + 32*kb + 8*(e/4) + 4*hl + e%4 of query my_q.
-    const bool need_mask = kGeneral || (kv0 + KT > N) || (kCausal && kv0 + KT - 1 > q_row0);
-    const int base = kv0 + 4 * hl;
     const FA2_LDS int* tsg = (const FA2_LDS int*)segk_ + buf * 64;
+    bool need_mask = (kv0 + KT > N) || (kCausal && kv0 + KT - 1 > q_row0);
+    if constexpr (kGeneral) {
+      // (wave-uniform) every pair of the 32 rows x KT keys visible: all keys
+      // below N (rows past N are not stored), the keys all in the prefix or the
+      // window satisfied at the block's corners, and under segment ids one id
+      // for all of them.
+      bool full = kv0 + KT <= N && (kv0 + KT - 1 < a.prefix || ((a.wl < 0 || kv0 >= q_row0 + 31 - a.wl) &&
+                                                                (a.wr < 0 || kv0 + KT - 1 <= q_row0 + a.wr)));
+      if constexpr (kSeg) {
+        if (full) full = rows_one_seg && __all(tsg[lane % KT] == seg_w);
+      }
+      need_mask = !full;
+    }
+    const int base = kv0 + 4 * hl;
     uint32_t pd[KT / 32][8];
 #pragma unroll
     for (int kb = 0; kb < KT / 32; ++kb) {

@@ -445,7 +445,7 @@ def main() -> int:
                     help="forward or gradient pass: split each sequence into this many equal contiguous documents")
     ap.add_argument("--fp8", action="store_true",
                     help="forward pass with Q and K in fp8 (e4m3, per-head scales) and V, O in the workload's "
-                         "16-bit type (head dim 128)")
+                         "16-bit type (head dims 64, 128, 256; with or without a mask)")
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "decode"), default="fwd",
                     help="time the forward pass (the headline), the gradient pass of the workload, or decode "
                          "against a key/value cache (a decode workload)")
@@ -483,9 +483,6 @@ def main() -> int:
         return 2
     if args.pass_ != "fwd" and args.fp8:
         log("fp8 inputs apply to the forward pass only")
-        return 2
-    if args.fp8 and (args.window is not None or args.prefix > 0 or args.documents > 0):
-        log("the fp8 forward pass takes no mask or the causal mask")
         return 2
     if args.pass_ == "decode":
         return run_decode(args)
@@ -529,10 +526,12 @@ def main() -> int:
         del dq, dk, dv
 
         def step():
-            fa.forward_fp8(dq8, dk8, dv16, ddq, ddk, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
-        flop = flop_count(w.B, w.H, w.N, w.d, w.causal)
-        metric = ("attention fwd TFLOP/s with fp8 (e4m3) Q, K and 16-bit V, % of the MI355X MFMA ceiling for "
-                  "half fp8, half fp16/bf16 products")
+            fa.forward_fp8(dq8, dk8, dv16, ddq, ddk, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream,
+                           **mask_kw)
+        flop = 4.0 * w.B * w.H * w.d * pairs if masked else flop_count(w.B, w.H, w.N, w.d, w.causal)
+        metric = ("attention fwd TFLOP/s with fp8 (e4m3) Q, K and 16-bit V" +
+                  (" over visible pairs (general mask)" if masked else "") +
+                  ", % of the MI355X MFMA ceiling for half fp8, half fp16/bf16 products")
         peak = PEAK_FP8_QK_TFLOPS
         # the oracle timing below runs on the real (descaled) inputs
         q = q8.to(torch.float64) * dsq.to(torch.float64).reshape(w.B, w.H, 1, 1)

@@ -475,8 +475,7 @@ def forward_fp8(q8, k8, v, descale_q=None, descale_k=None, causal: bool = False,
     d], d = 64, 128 or 256) and V in fp16 or bf16.  The real inputs are ``q8 * descale_q[b*H + h]``
     and ``k8 * descale_k[b*H + h]`` (``descale_*``: float32 [B*H] device tensors,
     or None for ones).  ``window``, ``prefix`` and ``segment_ids`` give a general
-    mask, as for ``forward`` (head dims 64 and 128; at 256 no mask or the causal
-    mask).  Returns ``(o, lse)`` with ``o`` in V's dtype."""
+    mask, as for ``forward``.  Returns ``(o, lse)`` with ``o`` in V's dtype."""
     import torch
 
     if not (q8.shape == k8.shape == v.shape) or q8.dim() != 4:

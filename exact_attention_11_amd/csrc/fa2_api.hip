@@ -640,8 +640,6 @@ int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, flo
       return FA2_ERR_ALIAS;
   }
   const FoldedMask f = fold_mask(m, N);
-  // Head dim 256 in fp8 runs on the pair kernel: no mask or the causal mask.
-  if (d == 256 && f.mode != fa2::kMaskNone && f.mode != fa2::kMaskCausal) return FA2_ERR_MASK;
 
   // ---- device ---------------------------------------------------------------
   const int dev_status = check_device();
@@ -669,12 +667,9 @@ int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, flo
   } else if (d == 128) {
     e = dtype == FA2_DTYPE_FP16 ? launch_m<fa2::kFp8Fp16, 128>(args, f.mode, s)
                                 : launch_m<fa2::kFp8Bf16, 128>(args, f.mode, s);
-  } else if (f.mode == fa2::kMaskCausal) {
-    e = dtype == FA2_DTYPE_FP16 ? launch<fa2::kFp8Fp16, 256, fa2::kMaskCausal>(args, s)
-                                : launch<fa2::kFp8Bf16, 256, fa2::kMaskCausal>(args, s);
   } else {
-    e = dtype == FA2_DTYPE_FP16 ? launch<fa2::kFp8Fp16, 256, fa2::kMaskNone>(args, s)
-                                : launch<fa2::kFp8Bf16, 256, fa2::kMaskNone>(args, s);
+    e = dtype == FA2_DTYPE_FP16 ? launch_m<fa2::kFp8Fp16, 256>(args, f.mode, s)
+                                : launch_m<fa2::kFp8Bf16, 256>(args, f.mode, s);
   }
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;

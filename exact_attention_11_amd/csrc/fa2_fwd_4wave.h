@@ -24,6 +24,8 @@
 // chunks, both for conflict-free reads.
 #pragma once
 
+#include <type_traits>
+
 #include "fa2_common.h"
 
 namespace fa2 {
@@ -62,6 +64,21 @@ __device__ __forceinline__ void load_k_tile(const uint16_t* __restrict__ kh, FA2
     dma16(kh + (int64_t)grow * D + (b % CPR) * 8, dst + q * 512);
   }
 }
+// The same for an e4m3 K tile (D bytes per row, CPR = D / 16 chunks).
+template <int D>
+__device__ __forceinline__ void load_k_tile_fp8(const char* __restrict__ kh, FA2_LDS uint16_t* dst, int kv0, int N,
+                                                int wave, int lane) {
+  constexpr int CPR = D / 16;
+  constexpr int kPerWave = kBc * CPR / (64 * kWaves);
+#pragma unroll
+  for (int t = 0; t < kPerWave; ++t) {
+    const int q = t * kWaves + wave;
+    const int b = 4 * q + (lane >> 4);
+    const int row = 16 * (b / CPR) + (lane & 15);
+    const int grow = min(kv0 + row, N - 1);
+    dma16(kh + (int64_t)grow * D + (b % CPR) * 16, dst + q * 512);
+  }
+}
 
 // The same for a V tile (row-major, swizzled): each instruction of a wave fills
 // 64 consecutive 16-byte LDS slots; slot s holds logical chunk
@@ -87,12 +104,19 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   constexpr bool kCausal = kMask == kMaskCausal;
   constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
   constexpr bool kSeg = kMask == kMaskSegments;
-  typedef Elem<kDType> E;
+  // fp8 instances: S = K Q^T on the fp8 MFMA from e4m3 Q and K (one byte per
+  // element); V, P and O stay 16-bit.
+  constexpr bool kQK8 = kDType == kFp8Fp16 || kDType == kFp8Bf16;
+  typedef Elem<kDType & 1> E;
   typedef typename E::V8 V8;
-  constexpr int CPR = D / 8;
-  constexpr int KS = D / 16;  // MFMA k-steps of S = K Q^T
+  typedef std::conditional_t<kQK8, i32x8, V8> QF;  // one S operand fragment of Q
+  constexpr int kEbK = kQK8 ? 1 : 2;                 // bytes per element of Q and K
+  constexpr int CPR = D / 8;                          // 16-byte chunks per V row
+  constexpr int CPRK = D * kEbK / 16;                 // 16-byte chunks per K row
+  constexpr int KS = kQK8 ? D / 64 : D / 16;          // MFMA k-steps of S = K Q^T
   constexpr int DB = D / 32;  // 32-wide blocks of the output columns
-  constexpr int kLoads = kBc * CPR / (64 * kWaves);
+  constexpr int kLoads = kBc * CPR / (64 * kWaves);    // V copies per wave per tile
+  constexpr int kLoadsK = kBc * CPRK / (64 * kWaves);  // K copies per wave per tile
   constexpr float kNegInf = -__builtin_huge_valf();
   static_assert(D == 256, "the four-wave kernel serves head dim 256");
 
@@ -106,7 +130,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   FA2_LDS int* const sSeg = (FA2_LDS int*)seg_;
   // Copies in flight per wave for one K tile: its rows, plus under segment ids
   // the keys' ids (copied by every wave, so the counts stay uniform).
-  constexpr int kKLoads = kLoads + (kSeg ? 1 : 0);
+  constexpr int kKLoads = kLoadsK + (kSeg ? 1 : 0);
 
   const int N = a.N;
   int bh, qtile;
@@ -121,7 +145,14 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   const int my_q = q_row0 + col;
   const int64_t head_off = (int64_t)bh * N * D;
   const uint16_t* __restrict__ kh = a.k + head_off;
+  const char* __restrict__ kh8 = (const char*)a.k + head_off;  // e4m3 K of this head
   const uint16_t* __restrict__ vh = a.v + head_off;
+  // Score multiplier in log2 units (the fp8 instances fold in the descales).
+  float c2 = a.c2;
+  if constexpr (kQK8) {
+    if (a.descale_q) c2 *= a.descale_q[bh];
+    if (a.descale_k) c2 *= a.descale_k[bh];
+  }
 
   // Key tiles: step st of the loop visits tile tile_of(st), st < nt (as in the
   // eight-wave kernel: tiles 0 .. nt-1 without a general mask, the runs of
@@ -163,7 +194,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   }
 
   auto load_k = [&](int kv0, int st) __attribute__((always_inline)) {
-    load_k_tile<D>(kh, sK, kv0, N, wave, lane);
+    if constexpr (kQK8) load_k_tile_fp8<D>(kh8, sK, kv0, N, wave, lane);
+    else load_k_tile<D>(kh, sK, kv0, N, wave, lane);
     if constexpr (kSeg) dma4(segb + min(kv0 + lane, N - 1), sSeg + (st & 1) * kBc);
   };
 
@@ -174,8 +206,19 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   // Q fragments (B operand of S^T = K Q^T), loaded once and kept in registers.
   // They are consumed right here so that the compiler's own wait for them
   // happens once, outside the loop (it also covers the two tile copies above).
-  V8 qf[KS];
-  {
+  QF qf[KS];
+  if constexpr (kQK8) {
+    // Lane (hl, col): bytes 64 ks + 32 hl .. + 31 of its query row.
+    const char* qp = (const char*)a.q + head_off + (int64_t)min(my_q, N - 1) * D + 32 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 lo = *(const u32x4*)(qp + 64 * ks);
+      const u32x4 hi = *(const u32x4*)(qp + 64 * ks + 16);
+      // (two 128-bit operands: a 256-bit "v" operand is invalid for the host pass)
+      asm volatile("" ::"v"(lo), "v"(hi));
+      qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  } else {
     const uint16_t* qp = a.q + head_off + (int64_t)min(my_q, N - 1) * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(qp + 16 * ks));
@@ -198,10 +241,19 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
   constexpr int kPipe = 4;
   V8 fr[kPipe];
   // S^T = K Q^T, fragment f: key block kb = f % 2, k-step ks = f / 2; lane
-  // (hl, col) reads row 32 kb + col, chunk 2 ks + hl of the K tile.
-  const uint32_t kbase = opaque_vgpr((uint32_t)(size_t)sK + (uint32_t)(((((col >> 4) * CPR) + hl) << 8) + ((col & 15) << 4)));
+  // (hl, col) reads row 32 kb + col, chunk 2 ks + hl of the K tile.  e4m3: an
+  // operand is two 16-byte halves, fragments f = 2 m + h with kb = m % 2,
+  // ks = m / 2, chunk 4 ks + 2 hl + h.
+  const uint32_t kbase = opaque_vgpr((uint32_t)(size_t)sK +
+                                     (uint32_t)(((((col >> 4) * CPRK) + (kQK8 ? 2 * hl : hl)) << 8) + ((col & 15) << 4)));
   auto k_frag = [&](int f) __attribute__((always_inline)) {
-    const uint32_t ad = kbase + (uint32_t)(((2 * (f & 1) * CPR) + 2 * (f >> 1)) << 8);
+    uint32_t ad;
+    if constexpr (kQK8) {
+      const int m = f >> 1;
+      ad = kbase + (uint32_t)(((2 * (m & 1) * CPRK) + 4 * (m >> 1) + (f & 1)) << 8);
+    } else {
+      ad = kbase + (uint32_t)(((2 * (f & 1) * CPRK) + 2 * (f >> 1)) << 8);
+    }
     return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(size_t)ad);
   };
   // O^T += V^T P^T, fragment f: key block c = f / DB, output block db = f % DB.
@@ -227,7 +279,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
     const u32x2 w2 = __builtin_bit_cast(u32x2, t2);
     return __builtin_bit_cast(V8, u32x4{w1[0], w1[1], w2[0], w2[1]});
   };
-  constexpr int kNs = 2 * KS;             // S fragments
+  constexpr int kNs = kQK8 ? 4 * KS : 2 * KS;  // S fragments
   constexpr int kNpv = (kBc / 16) * DB;   // P.V fragments
 
   for (int st = 0; st < nt; ++st) {
@@ -251,8 +303,23 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
       for (int i = 0; i < kPipe; ++i) fr[i] = k_frag(i);
 #pragma unroll
       for (int f = 0; f < kNs; ++f) {
-        s[f & 1] = E::mfma(fr[f % kPipe], qf[f >> 1], s[f & 1]);
-        if (f + kPipe < kNs) fr[f % kPipe] = k_frag(f + kPipe);
+        if constexpr (kQK8) {
+          // An fp8 MFMA takes the fragment pair (f - 1, f): issue it on the
+          // second half, and reload the pair's slots only then.
+          if (f & 1) {
+            const int m = f >> 1;
+            const u32x4 lo = __builtin_bit_cast(u32x4, fr[(f - 1) % kPipe]);
+            const u32x4 hi = __builtin_bit_cast(u32x4, fr[f % kPipe]);
+            const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            s[m & 1] = mfma_fp8(ka, qf[m >> 1], s[m & 1]);
+            if (f - 1 + kPipe < kNs) fr[(f - 1) % kPipe] = k_frag(f - 1 + kPipe);
+            if (f + kPipe < kNs) fr[f % kPipe] = k_frag(f + kPipe);
+          }
+        } else {
+          s[f & 1] = E::mfma(fr[f % kPipe], qf[f >> 1], s[f & 1]);
+          if (f + kPipe < kNs) fr[f % kPipe] = k_frag(f + kPipe);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -275,11 +342,11 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
       }
       if (!seg_all) need_mask = true;
     }
-    const bool generic = need_mask || !(a.c2 > 0.f);
+    const bool generic = need_mask || !(c2 > 0.f);
 
     uint32_t pk[2][8];  // probabilities, packed pairs, B-operand order
     if (active) {
-      float mul = a.c2;
+      float mul = c2;
       if (generic) {
         // Scale first, then mask: t = -inf for keys past N or after the query.
 #pragma unroll
@@ -298,7 +365,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fa2_fwd_4wave(FwdA
                        !(key < a.prefix || ((a.wl < 0 || key >= my_q - a.wl) && (a.wr < 0 || key <= my_q + a.wr)));
               if (kSeg && !seg_all) masked = masked || (int)sg[r >> 2][r & 3] != seg_q;
             }
-            const float t = s[kb][r] * a.c2;
+            const float t = s[kb][r] * c2;
             s[kb][r] = masked ? kNegInf : t;
           }
         }

@@ -286,8 +286,7 @@ int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse
  * with M the mask of fa2_fwd_masked (sliding window, prefix, segment ids; the
  * mask as a 0 / -inf score term: "Flash Attention 2", section "Causal
  * masking").  Arguments, layout, ownership and errors as for fa2_fwd_fp8, plus
- * FA2_ERR_MASK (as for fa2_fwd_masked, and for a mask other than none or
- * causal at d = 256); segment_ids must not overlap o or lse.
+ * FA2_ERR_MASK (as for fa2_fwd_masked); segment_ids must not overlap o or lse.
  * fa2_fwd_fp8(..., causal, ...) is this call with {causal, -1, -1, 0, NULL}.
  */
 int fa2_fwd_fp8_masked(const void* q, const void* k, const void* v, void* o, float* lse,

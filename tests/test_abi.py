@@ -371,9 +371,6 @@ def test_fp8_masked_shared_checks(lib):
     # the checks fa2_fwd_fp8 makes apply to the masked entry as well
     m = fa.Fa2Mask(1, 4, 0, 2, None)
     assert _fp8_masked(m, d=512) == fa.FA2_ERR_HEADDIM
-    # head dim 256 in fp8: no mask or the causal mask only
-    assert _fp8_masked(m, d=256) == fa.FA2_ERR_MASK
-    assert _fp8_masked(fa.Fa2Mask(0, -1, -1, 0, 0xB0000000), d=256) == fa.FA2_ERR_MASK
     assert _fp8_masked(m, dtype=2) == fa.FA2_ERR_DTYPE
     assert _fp8_masked(m, o=Q) == fa.FA2_ERR_ALIAS
     assert _fp8_masked(m, dq=DQS + 2) == fa.FA2_ERR_ALIGN
@@ -388,9 +385,10 @@ def test_fp8_masked_valid_call_without_device_reports_device_error(lib):
     for mask in (None, fa.Fa2Mask(1, 5, 0, 3, 0xB0000000), fa.Fa2Mask(0, 7, 2, 0, None)):
         for dtype in (0, 1):
             assert _fp8_masked(mask, dtype=dtype, N=333) == fa.FA2_ERR_DEVICE
-    # masks that reduce to none or causal are accepted at head dim 256
-    for mask in (fa.Fa2Mask(1, -1, -1, 0, None), fa.Fa2Mask(0, 400, 400, 0, None), fa.Fa2Mask(0, -1, 0, 0, None)):
-        assert _fp8_masked(mask, d=256, N=333) == fa.FA2_ERR_DEVICE
+    for mask in (None, fa.Fa2Mask(1, -1, -1, 0, None), fa.Fa2Mask(1, 5, 0, 3, 0xB0000000),
+                 fa.Fa2Mask(0, 7, 2, 0, None)):
+        for d in (64, 256):
+            assert _fp8_masked(mask, d=d, N=333) == fa.FA2_ERR_DEVICE
 
 
 def test_python_fp8_forward_rejects_bad_tensors(lib):

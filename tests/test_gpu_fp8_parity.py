@@ -175,10 +175,11 @@ def test_fp8_head_dim_256_full_size_sampled():
     _log(f"  worst max|dO| over {B * H} heads: {worst:.3e}")
 
 
-def test_fp8_head_dim_256_rejects_general_masks():
+def test_fp8_mask_argument_errors():
+    """A malformed mask is an error of the fp8 entry point too."""
     q8, k8, v, dq, dk = make_qkv_fp8(1, 2, 100, 256, torch.float16, "normal", 1)
     with pytest.raises(fa.Fa2Error) as e:
-        fa.forward_fp8(q8.cuda(), k8.cuda(), v.cuda(), window=(10, 0))
+        fa.forward_fp8(q8.cuda(), k8.cuda(), v.cuda(), window=(-3, 0))
     assert e.value.status == fa.FA2_ERR_MASK
 
 
@@ -280,7 +281,7 @@ def _masked_case(B, H, N, v_dtype, mask_name, seed=0, d=128):
 
 @pytest.mark.parametrize("mask_name", sorted(FP8_MASKS))
 @pytest.mark.parametrize("v_dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fp8_masked_parity(d, v_dtype, mask_name):
     """700 rows: three query tiles per head, two runs of key tiles under a
     prefix, a ragged last tile."""
@@ -289,12 +290,12 @@ def test_fp8_masked_parity(d, v_dtype, mask_name):
 
 @pytest.mark.parametrize("mask_name", ["prefix_causal_window", "docs_prefix_window"])
 @pytest.mark.parametrize("N", [1, 2, 65, 257])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fp8_masked_parity_short(d, N, mask_name):
     _masked_case(1, 2, N, torch.float16, mask_name, seed=7, d=d)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fp8_masked_reductions_match_plain_entry(d):
     """Masks that reduce to none or causal take the plain fp8 instances: bitwise
     the same as fa2_fwd_fp8."""

@@ -47,7 +47,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # The sources that define the kernels of each pass (a recorded profile applies
 # while their digest is unchanged).
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
-                  for f in ("fa2_common.h", "fa2_fwd_4wave.h", "fa2_fwd_8wave.h", "fa2_fwd_pair.h", "fa2_fwd_w64.h")]
+                  for f in ("fa2_common.h", "fa2_fwd_8wave.h", "fa2_fwd_pair.h", "fa2_fwd_w64.h")]
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)
                       for f in ("fa2_common.h", "fa2_bwd.h")]
 DECODE_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_11_amd", "csrc", f)

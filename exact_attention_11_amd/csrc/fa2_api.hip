@@ -15,7 +15,6 @@
 #include "fa2.h"
 #include "fa2_bwd.h"
 #include "fa2_decode.h"
-#include "fa2_fwd_4wave.h"
 #include "fa2_fwd_8wave.h"
 #include "fa2_fwd_pair.h"
 #include "fa2_fwd_w64.h"
@@ -102,7 +101,7 @@ void set_mask_args(fa2::FwdArgs& args, const FoldedMask& f, const fa2_mask& m, i
 }
 
 // Query rows per workgroup of the kernel that serves head dim d.
-int64_t rows_per_workgroup(int64_t d) { return d == 256 ? fa2::w4::kBr : fa2::w8::kBr; }
+int64_t rows_per_workgroup(int64_t d) { return d == 256 ? fa2::pr::kBr : fa2::w8::kBr; }
 
 // One workgroup's sample for fa2_clock_sample: its XCD, its HW_ID (which CU),
 // that CU's shader-clock counter and the real-time counter.  Thread 0 writes
@@ -124,13 +123,9 @@ __global__ void fa2_clock_kernel(uint64_t* out) {
 
 template <int kDType, int D, int kMask>
 hipError_t launch(const fa2::FwdArgs& args, hipStream_t stream) {
-  if constexpr (D == 256 && (kMask == fa2::kMaskNone || kMask == fa2::kMaskCausal)) {
-    static_assert(fa2::pr::kBr == fa2::w4::kBr, "both head-dim-256 kernels take the same query tiles");
+  if constexpr (D == 256) {
     hipLaunchKernelGGL((fa2::pr::fa2_fwd_pair<kDType, kMask>), dim3(args.n_wg), dim3(fa2::pr::kThreads), 0, stream,
                        args);
-  } else if constexpr (D == 256) {
-    hipLaunchKernelGGL((fa2::w4::fa2_fwd_4wave<kDType, D, kMask>), dim3(args.n_wg), dim3(fa2::w4::kThreads), 0,
-                       stream, args);
   } else if constexpr (D == 128 && (kDType == fa2::kFp16 || kDType == fa2::kBf16) &&
                        (kMask == fa2::kMaskNone || kMask == fa2::kMaskCausal)) {
     static_assert(fa2::w64::kBr == fa2::w8::kBr, "both head-dim-128 kernels take the same query tiles");

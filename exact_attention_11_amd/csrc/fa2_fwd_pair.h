@@ -12,6 +12,11 @@
 //    "Method"; "6.2 FlashAttention V2 in depth", sections 3.2, 6.1, 7.1).
 //  * Causal block classes: key tiles past the query tile are never visited,
 //    tiles crossing the diagonal are masked element by element (section 5.3).
+//    General masks (sliding window, a prefix visible to every query, document
+//    segment ids: "Flash Attention 2", section "Causal masking") likewise: the
+//    key tiles the rows can see come in at most two runs (the prefix, the
+//    window), cut to the span of matching segment ids, and the keys a wavefront
+//    cannot see are masked element by element.
 //  * Head dims up to 256 ("FlashAttention-2: ...", "Limitations & open
 //    questions").
 //
@@ -71,7 +76,8 @@ __device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
 template <int kDType, int kMask>
 __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   constexpr bool kCausal = kMask == kMaskCausal;
-  static_assert(kMask == kMaskNone || kMask == kMaskCausal, "no mask or the causal mask");
+  constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
+  constexpr bool kSeg = kMask == kMaskSegments;
   // fp8 instances: S = K Q^T on the fp8 MFMA from e4m3 Q and K (one byte per
   // element); V, P and O stay 16-bit.
   constexpr bool kQK8 = kDType == kFp8Fp16 || kDType == kFp8Bf16;
@@ -99,10 +105,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   FA2_LDS uint16_t* const sV = (FA2_LDS uint16_t*)sV_;
   FA2_LDS uint32_t* const sP = (FA2_LDS uint32_t*)sP_;
   FA2_LDS float* const sM = (FA2_LDS float*)sM_;
+  // Under segment ids: the keys' ids of the two K slots, and the span reduction.
+  __shared__ __attribute__((aligned(16))) int seg_[kSeg ? 2 * kBc : 4];
+  __shared__ int red_[kSeg ? 2 * kWaves : 2];
+  FA2_LDS int* const sSeg = (FA2_LDS int*)seg_;
 
   const int N = a.N;
   int bh, qtile;
-  wg_to_tile(a, kCausal, bh, qtile);
+  wg_to_tile(a, kCausal || (kGeneral && a.grow), bh, qtile);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -129,8 +139,45 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   // skips its products and softmax and only issues its share of the copies.
   const bool live = q_row0 < N;
 
-  const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
-  const int nt = (kv_end + kBc - 1) / kBc;
+  // Key tiles: step st visits tile tile_of(st), st < nt.  Without a general
+  // mask tiles 0 .. nt-1 (under the causal mask up to the rows' last key); a
+  // general mask visits the runs of general_runs, cut to the keys whose segment
+  // ids can match.
+  int nt, run_a0 = 0, run_na = 0, run_b0 = 0;
+  const int* __restrict__ segb = nullptr;  // this batch's segment ids
+  int seg_q = 0;                           // this lane's query's segment id
+  if constexpr (kGeneral) {
+    const int q0 = qtile * kBr, q1 = min(N, q0 + kBr) - 1;
+    int kf = 0, kl = N - 1;
+    if constexpr (kSeg) {
+      segb = a.seg + (int64_t)(bh / a.H) * N;
+      seg_q = segb[min(my_q, N - 1)];
+      const TileRuns all = general_runs(a, q0, q1, 0, N - 1, kBc);
+      const int lo = all.na > 0 ? 0 : all.b0 * kBc;
+      const int hi = min(N - 1, (all.b0 + all.nb) * kBc - 1);
+      segment_span<kWaves>(segb, q0, q1, lo, hi, (FA2_LDS int*)red_, kf, kl);
+    }
+    const TileRuns r = general_runs(a, q0, q1, kf, kl, kBc);
+    run_a0 = r.a0;
+    run_na = r.na;
+    run_b0 = r.b0;
+    nt = r.na + r.nb;
+  } else {
+    const int kv_end = kCausal ? min(N, (qtile + 1) * kBr) : N;
+    nt = (kv_end + kBc - 1) / kBc;
+  }
+  auto tile_of = [&](int step) __attribute__((always_inline)) {
+    if constexpr (kGeneral) return step < run_na ? run_a0 + step : run_b0 + (step - run_na);
+    else return step;
+  };
+  // Under segment ids: when the pair's 32 rows share one id (seg_w), a block's
+  // visibility follows from a comparison of each key's id with it.
+  bool rows_one_seg = false;
+  int seg_w = 0;
+  if constexpr (kSeg) {
+    seg_w = __builtin_amdgcn_readfirstlane(seg_q);
+    rows_one_seg = __all(seg_q == seg_w);
+  }
 
   // Copies: 64 KB per step through the CU's load path, which takes in the
   // order of 2000 cycles to accept them when they are issued all at once, and
@@ -159,9 +206,11 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   const int vrow = 2 * cw + (lane >> 5);
   const int vch = (lane & 31) ^ swz_v(vrow);
   const uint32_t voffV = (uint32_t)((vrow * D + vch * 8) * 2);
-  // Copy instruction t of K tile `tile` into `slot`.
+  // Copy instruction t of K tile `tile` into `slot` (under segment ids, with
+  // the first one, wave 0 also copies the keys' ids).
   auto issue_k1 = [&](int tile, int slot, int t) __attribute__((always_inline)) {
     const int kv0 = tile * kBc;
+    if (kSeg && t == 0 && wave == 0) dma4(segb + min(kv0 + lane, N - 1), sSeg + slot * kBc);
     FA2_LDS uint16_t* dk = sK + slot * kTile + (t * kCopyWaves + cw) * 512;
     if constexpr (kQK8) {
       if (kv0 + kBc <= N) {
@@ -202,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
   // P.V with zero weights on V slot 1 and the partners' weights in LDS, so
   // both start as zeros (finite values: a zero weight times garbage could be
   // NaN); they are visible after the first barrier.
-  if (grp == 0) issue_k(0, 0);
+  if (grp == 0) issue_k(tile_of(0), 0);
   {
     FA2_LDS u32x4* zv = (FA2_LDS u32x4*)(sV + kTile);
 #pragma unroll
@@ -347,17 +396,48 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
       }
       if (i + kPipe < kNs + kNpv && !(kQK8 && i < kNs && (i & 1) == 0)) fr[i % kPipe] = load_op(kbase, vb, i + kPipe);
       if (copy_k && i >= kNs && ((i - kNs) % kCopyStride) == 0 && k_next)
-        issue_k1(st + 1, (st + 1) & 1, (i - kNs) / kCopyStride);
+        issue_k1(tile_of(st + 1), (st + 1) & 1, (i - kNs) / kCopyStride);
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
     s = sa;
-    const int k0 = st * kBc + 32 * kh;  // this wavefront's first key
-    const bool need_mask = k0 + 31 >= N || (kCausal && k0 + 31 > q_row0);
+    const int k0 = tile_of(st) * kBc + 32 * kh;  // this wavefront's first key
+    bool need_mask = k0 + 31 >= N || (kCausal && k0 + 31 > q_row0);
+    if constexpr (kGeneral) {
+      // (wave-uniform) every pair of the 32 rows x 32 keys visible: all keys
+      // below N, the keys all in the prefix or the window satisfied at the
+      // block's corners, and under segment ids one id for all of them.
+      const int k1 = k0 + 31, qa = q_row0, qb = q_row0 + 31;
+      bool full = k1 < N && (k1 < a.prefix || ((a.wl < 0 || k0 >= qb - a.wl) && (a.wr < 0 || k1 <= qa + a.wr)));
+      if constexpr (kSeg) {
+        if (full) full = rows_one_seg && __all(sSeg[(st & 1) * kBc + 32 * kh + col] == seg_w);
+      }
+      need_mask = !full;
+    }
     // Key of score r of this lane: k0 + 8 (r / 4) + 4 hl + r % 4.
     int lim = N - (k0 + 4 * hl);
     if (kCausal) lim = min(lim, my_q + 1 - (k0 + 4 * hl));
-    if (pos) {
+    if (kGeneral && need_mask) {
+      // Score r is key base + off, off = 8 (r / 4) + r % 4: visible iff below N
+      // and in the prefix or the window (and, under segment ids, of the row's id).
+      const int base = k0 + 4 * hl;
+      const int lim_p = a.prefix - base;
+      const int lo_w = a.wl < 0 ? INT32_MIN / 2 : my_q - a.wl - base;
+      const int hi_w = a.wr < 0 ? INT32_MAX / 2 : my_q + a.wr - base;
+      u32x4 sg[4] = {};
+      if constexpr (kSeg) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) sg[g4] = *(const FA2_LDS u32x4*)(sSeg + (st & 1) * kBc + 32 * kh + 8 * g4 + 4 * hl);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        bool ok = off < lim && (off < lim_p || (off >= lo_w && off <= hi_w));
+        if constexpr (kSeg) ok = ok && (int)sg[r >> 2][r & 3] == seg_q;
+        const float tt = pos ? s[r] : s[r] * c2;
+        s[r] = ok ? tt : kNegInf;
+      }
+    } else if (pos) {
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3)) < lim ? s[r] : kNegInf;
@@ -422,9 +502,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
       wait_vm_lds_barrier<0>();
       __builtin_amdgcn_sched_barrier(0);
       if (grp == 0) {
-        if (st + 1 < nt) issue_k(st + 1, (st + 1) & 1);
+        if (st + 1 < nt) issue_k(tile_of(st + 1), (st + 1) & 1);
       } else {
-        if (st < nt) issue_v(st, st & 1);
+        if (st < nt) issue_v(tile_of(st), st & 1);
       }
       lds_done_barrier();
     }
@@ -444,7 +524,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_fwd_pair(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       wait_vm_lds_barrier<0>();
       __builtin_amdgcn_sched_barrier(0);
-      if (st < nt) issue_v(st, st & 1);
+      if (st < nt) issue_v(tile_of(st), st & 1);
       if (st > 0) softmax();
       __builtin_amdgcn_sched_barrier(0);
       lds_done_barrier();

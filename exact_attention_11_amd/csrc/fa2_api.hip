@@ -165,12 +165,20 @@ hipError_t launch_bwd(const fa2::bwd::BwdArgs& args, hipStream_t stream) {
                      0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa2_bwd_dkdv<kDType, D, kMask>), dim3((unsigned)(args.n_kv_wg * args.BH)), dim3(kThreads), 0,
-                     stream, args);
+  if constexpr (D == 256)
+    hipLaunchKernelGGL((fa2_bwd_dkdv_pair<kDType, kMask>), dim3((unsigned)(args.n_kv_wg * args.BH)),
+                       dim3(kPairThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((fa2_bwd_dkdv<kDType, D, kMask>), dim3((unsigned)(args.n_kv_wg * args.BH)), dim3(kThreads), 0,
+                       stream, args);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa2_bwd_dq<kDType, D, kMask>), dim3((unsigned)(args.n_q_wg * args.BH)), dim3(kThreads), 0,
-                     stream, args);
+  if constexpr (D == 256)
+    hipLaunchKernelGGL((fa2_bwd_dq_pair<kDType, kMask>), dim3((unsigned)(args.n_q_wg * args.BH)),
+                       dim3(kPairThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((fa2_bwd_dq<kDType, D, kMask>), dim3((unsigned)(args.n_q_wg * args.BH)), dim3(kThreads), 0,
+                       stream, args);
   return hipGetLastError();
 }
 

@@ -32,6 +32,10 @@
 //    dK^T += Q^T dS directly as B operands; the A operands (dO^T, Q^T) come
 //    from the same LDS tiles through ds_read_b64_tr_b16, reading the query rows
 //    in the order the accumulator holds them.
+//  * fa2_bwd_dkdv_pair (d = 256): the same product chain over eight
+//    wavefronts, two per block of 32 keys: one holds K and forms S, P and dV,
+//    the other holds V and forms dP, dS and dK, with P passed between them
+//    through LDS, so that neither needs more than 256 registers.
 //  * fa2_bwd_dq: the forward's layout: S^T = K Q^T and dP^T = V dO^T with Q and
 //    dO of the wave's 32 rows in registers and K, V tiles in LDS; a lane holds
 //    one query, so L and D are per-lane scalars; dQ^T += K^T dS^T reads K^T
@@ -53,14 +57,13 @@ constexpr int kQTile = 64;               // fa2_bwd_dkdv: query rows per streame
 constexpr int kRowsPerWg = 32 * kWaves;  // fa2_bwd_dq: query rows per workgroup
 constexpr int kKTile = 64;               // fa2_bwd_dq: keys per streamed tile
 constexpr int kDeltaRows = 16;           // fa2_bwd_delta: rows per workgroup (16 lanes each)
-// Workgroups per CU each kernel is compiled for: two (two wavefronts per SIMD,
-// at most 256 registers each) up to d = 128, so that one workgroup's products
-// overlap the other's softmax gradient and memory waits; one at d = 256, where
-// the accumulators alone take 256 registers.  (At d = 128 fa2_bwd_dkdv then
-// needs 255 registers, and fits them only because its LDS operand offsets are
-// formed at each use; see the lane values in its loop.)
-template <int D> constexpr int kDkdvWgPerCu = D <= 128 ? 2 : 1;
-template <int D> constexpr int kDqWgPerCu = D <= 128 ? 2 : 1;
+// fa2_bwd_dkdv and fa2_bwd_dq (d = 64, 128) are compiled for two workgroups
+// per CU (two wavefronts per SIMD, at most 256 registers each), so that one
+// workgroup's products overlap the other's softmax gradient and memory waits.
+// (At d = 128 fa2_bwd_dkdv then needs 255 registers, and fits them only because
+// its LDS operand offsets are formed at each use; see the lane values in its
+// loop.)  At d = 256 the gradients come from fa2_bwd_dkdv_pair and
+// fa2_bwd_dq_pair, which split each block's work between two wavefronts.
 
 struct BwdArgs {
   const uint16_t* q;
@@ -136,13 +139,13 @@ __device__ __forceinline__ const void* sgpr_base(const void* p) {
 // compiler cannot prove it (the general-mask kernels' tile bounds, which pass
 // through an LDS reduction under segment ids and through a local argument
 // block otherwise), so the base goes to scalar registers through sgpr_base.
-template <int D, int R, bool kVBase = false>
+template <int D, int R, bool kVBase = false, int kNW = kWaves>
 __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2_LDS uint16_t* dst, int r0, int N,
                                           int wave, int lane) {
   constexpr int CPR = D / 8;
-  constexpr int kPer = R * CPR / (64 * kWaves);
-  constexpr int kStride = 64 * kWaves / CPR;  // rows between a wave's consecutive copies
-  static_assert(kPer * 64 * kWaves == R * CPR, "tile copy split");
+  constexpr int kPer = R * CPR / (64 * kNW);
+  constexpr int kStride = 64 * kNW / CPR;  // rows between a wave's consecutive copies
+  static_assert(kPer * 64 * kNW == R * CPR, "tile copy split");
   const uint16_t* base = head + (int64_t)r0 * D;
   if constexpr (kVBase) base = (const uint16_t*)sgpr_base(base);
   const int last = N - 1 - r0;  // rows past it re-read row N - 1
@@ -161,12 +164,12 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2
     const int row = s0 / CPR;
     const uint32_t off = (uint32_t)(row * D * 2 + (((s0 % CPR) ^ swz<D>(row)) << 4));
 #pragma unroll
-    for (int t = 0; t < kPer; ++t) dma16_sbase(base + t * kStride * D, off, dst + (t * kWaves + wave) * 64 * 8);
+    for (int t = 0; t < kPer; ++t) dma16_sbase(base + t * kStride * D, off, dst + (t * kNW + wave) * 64 * 8);
     return;
   }
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
-    const int s0 = (t * kWaves + wave) * 64;
+    const int s0 = (t * kNW + wave) * 64;
     const int s = s0 + ln;
     const int row = s / CPR;
     const int ch = (s % CPR) ^ swz<D>(row);
@@ -209,9 +212,10 @@ __global__ __launch_bounds__(256) void fa2_bwd_delta(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV of kKeysPerWg keys of one head; query tiles stream through LDS.
+// dK and dV of kKeysPerWg keys of one head (d = 64, 128); query tiles stream
+// through LDS.
 template <int kDType, int D, int kMask>
-__global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dkdv(BwdArgs a) {
   constexpr bool kCausal = kMask == kMaskCausal;
   constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
   constexpr bool kSeg = kMask == kMaskSegments;
@@ -219,27 +223,21 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
   typedef typename E::V8 V8;
   constexpr int KS = D / 16;  // k-steps of S = Q K^T over the head dim
   constexpr int DB = D / 32;  // 32-wide blocks of the head dim
-  // At d = 256 the dK/dV accumulators alone take 256 registers: V (the B
-  // operand of dP = dO V^T) is read from an LDS copy of the workgroup's keys
-  // instead of being held in 64 more, and Q and dO stream in 32-row tiles so
-  // that the copy fits.
-  constexpr bool kVLds = D == 256;
-  constexpr int QT = kVLds ? 32 : kQTile;  // query rows per streamed tile
+  static_assert(D == 64 || D == 128, "head dim 256: fa2_bwd_dkdv_pair");
+  constexpr int QT = kQTile;  // query rows per streamed tile
   constexpr int kTile = QT * D;
   constexpr int kStat = 64;  // floats per L or D row of the stat buffers (one copy of 64 lanes)
   constexpr int kNStat = kSeg ? 3 : 2;  // stat rows per buffer: L, D (and the rows' segment ids)
-  // Operand offsets formed at each use from a few lane values (below) from
-  // d = 128 on, where holding all of them across the loop costs spills.
+  // Operand offsets formed at each use from a few lane values (below) at
+  // d = 128, where holding all of them across the loop costs spills.
   constexpr bool kXorAddr = D >= 128;
 
   // [buffer][Q | dO] tiles, then [buffer][L | D] rows.
   __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];
   __shared__ __attribute__((aligned(1024))) float stat_[2][kNStat][kStat];
   __shared__ int red_[2 * kWaves];  // segment span reduction
-  __shared__ __attribute__((aligned(1024))) uint16_t vt_[kVLds ? kKeysPerWg * D : 8];
   FA2_LDS uint16_t* const sT = (FA2_LDS uint16_t*)smem_;
   FA2_LDS float* const sS = (FA2_LDS float*)&stat_[0][0][0];
-  FA2_LDS uint16_t* const sV = (FA2_LDS uint16_t*)vt_;
 
   const int N = a.N;
   // Key tiles with a low index see the most query tiles under the causal mask:
@@ -294,8 +292,6 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
       if constexpr (kSeg) dma4(segb + r, sS + (kNStat * buf + 2) * kStat);
     }
   };
-  // V of the workgroup's keys (d = 256), complete at the loop's first barrier.
-  if constexpr (kVLds) load_rows<D, kKeysPerWg, kGeneral>(a.v + head_off, sV, kt * kKeysPerWg, N, wave, lane);
   load_tile(it0, 0);
 
   // The segment id of this lane's key; whether the wave's 32 keys share one id.
@@ -307,7 +303,7 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
     keys_one_seg = seg_w == wave_max(seg_k);
   }
   // K and V of this lane's key (B operands of S = Q K^T and dP = dO V^T).
-  V8 kf[KS], vf[kVLds ? 1 : KS];
+  V8 kf[KS], vf[KS];
   {
     const int r = min(my_k, N - 1);
     const uint16_t* kp = a.k + head_off + (int64_t)r * D + 8 * hl;
@@ -315,7 +311,7 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(kp + 16 * ks));
-      if constexpr (!kVLds) vf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(vp + 16 * ks));
+      vf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(vp + 16 * ks));
     }
   }
 
@@ -354,10 +350,10 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
       // tile, chunk 2 ks + hl): the swizzle depends on r % 16 only, and
       // (2 ks + hl) ^ z = 2 ks ^ (hl ^ z), so chunk ks sits at
       // r * 2D + ((32 ks) ^ hz16).  Transposed reads (rows r1, r1 + 8, 4 head
-      // dims from 32 db + ...): likewise 64 db ^ w16.  From d = 128 on the
-      // offsets are formed at each use from five lane values derived here, in
-      // the loop, from an opaque lane index: held across the loop, the distinct
-      // offsets (48 at d = 256) would be spilled.
+      // dims from 32 db + ...): likewise 64 db ^ w16.  At d = 128 the offsets
+      // are formed at each use from five lane values derived here, in the
+      // loop, from an opaque lane index: held across the loop, the distinct
+      // offsets would be spilled.
       const int ln = kXorAddr ? (int)opaque_vgpr((uint32_t)lane) : lane;
       const int lcol = ln & 31, lhl = (ln >> 5) & 1, ltg = (ln >> 4) & 3, ltl = ln & 15;
       const uint32_t hz16 = (uint32_t)((lhl ^ swz<D>(lcol)) << 4);
@@ -377,13 +373,7 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
         const V8 aq = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)((const FA2_LDS char*)tq + off));
         const V8 ag = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)((const FA2_LDS char*)tg_ + off));
         s = E::mfma(aq, kf[ks], s);
-        if constexpr (kVLds) {
-          const uint32_t vo = (uint32_t)((wave * 32 + lcol) * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
-          const V8 bv = __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)((const FA2_LDS char*)sV + vo));
-          dp = E::mfma(ag, bv, dp);
-        } else {
-          dp = E::mfma(ag, vf[ks], dp);
-        }
+        dp = E::mfma(ag, vf[ks], dp);
       }
       // Element e of the accumulators is query q0 + 8*(e/4) + 4*hl + e%4 of this
       // lane's key; its L and D sit at the same offset in the stat rows.
@@ -486,9 +476,259 @@ __global__ __launch_bounds__(kThreads, kDkdvWgPerCu<D>) void fa2_bwd_dkdv(BwdArg
 }
 
 // ---------------------------------------------------------------------------
-// dQ of kRowsPerWg query rows of one head; key/value tiles stream through LDS.
+// dK and dV at head dim 256.  The dK and dV accumulators of 32 keys take 256
+// registers, so one wavefront holding both (with K as an operand) spills.
+// Here two wavefronts share each block of 32 keys and split the chain rule
+// between them:
+//  * wave kb (role 0) holds K of the keys, forms S = Q K^T, the probabilities
+//    P = exp(s - L) and accumulates dV^T += dO^T P;
+//  * wave kb + 4 (role 1) holds V, forms dP = dO V^T, takes P from role 0
+//    through LDS (fp32, so dS is formed from the same values as in a single
+//    wavefront), forms dS = P o (dP - D) and accumulates dK^T += Q^T dS.
+// Each holds 128 accumulators and a 64-register operand, so the eight
+// wavefronts run two per SIMD (the two of a pair on one SIMD when waves are
+// placed round-robin): one's elementwise work overlaps the other's products.
+// Per streamed tile of 32 query rows: the tile barrier, the first products and
+// role 0's probabilities, a barrier that publishes P, then role 1's dS and both
+// second products.  Every product and every rounding is the one the
+// single-wavefront kernel performs, in the same order.
+constexpr int kPairWaves = 8;
+constexpr int kPairThreads = 64 * kPairWaves;
+
+template <int kDType, int kMask>
+__global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) {
+  constexpr int D = 256;
+  constexpr bool kCausal = kMask == kMaskCausal;
+  constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
+  constexpr bool kSeg = kMask == kMaskSegments;
+  typedef Elem<kDType> E;
+  typedef typename E::V8 V8;
+  constexpr int KS = D / 16;  // k-steps of S = Q K^T and dP = dO V^T
+  constexpr int DB = D / 32;  // 32-wide blocks of the head dim
+  constexpr int QT = 32;      // query rows per streamed tile
+  constexpr int kTile = QT * D;
+  constexpr int kStat = 64;
+  constexpr int kNStat = kSeg ? 3 : 2;  // stat rows per buffer: L, D (and the rows' segment ids)
+  static_assert(kKeysPerWg == 4 * 32, "four key blocks per workgroup");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];  // [buffer][Q | dO]
+  __shared__ __attribute__((aligned(1024))) float stat_[2][kNStat][kStat];
+  __shared__ __attribute__((aligned(1024))) float xch_[4 * 64 * 16];  // P of each key block, per lane
+  __shared__ int red_[2 * kPairWaves];                                // segment span reduction
+  FA2_LDS uint16_t* const sT = (FA2_LDS uint16_t*)smem_;
+  FA2_LDS float* const sS = (FA2_LDS float*)&stat_[0][0][0];
+
+  const int N = a.N;
+  const int kt = blockIdx.x / a.BH;
+  const int bh = blockIdx.x - kt * a.BH;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = wave & 3;     // key block
+  const int role = wave >> 2;  // 0: S, P, dV; 1: dP, dS, dK
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int col = lane & 31;
+  const int kw0 = kt * kKeysPerWg + kb * 32;  // the pair's first key
+  const int my_k = kw0 + col;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const uint16_t* __restrict__ qh = a.q + head_off;
+  const uint16_t* __restrict__ gh = a.dout + head_off;
+  const float* __restrict__ lh = a.lse + (int64_t)bh * N;
+  const float* __restrict__ dh = a.delta + (int64_t)bh * N;
+  const int* __restrict__ segb = kSeg ? a.seg + (int64_t)(bh / a.H) * N : nullptr;
+
+  // Query tiles that see the workgroup's keys (as in fa2_bwd_dkdv).
+  int it0 = kCausal ? (kt * kKeysPerWg) / QT : 0;
+  int it1 = (N + QT - 1) / QT;
+  if constexpr (kGeneral) {
+    const int k0 = kt * kKeysPerWg, k1 = min(N - 1, k0 + kKeysPerWg - 1);
+    int lo = 0, hi = N - 1;
+    if (k0 >= a.prefix) {
+      if (a.wr >= 0) lo = max(0, k0 - a.wr);
+      if (a.wl >= 0) hi = min(N - 1, k1 + a.wl);
+    }
+    if constexpr (kSeg) {
+      int f, l;
+      segment_span<kPairWaves>(segb, k0, k1, lo, hi, (FA2_LDS int*)red_, f, l);
+      lo = max(lo, f);
+      hi = min(hi, l);
+    }
+    it0 = lo / QT;
+    it1 = hi / QT + 1;
+  }
+
+  auto load_tile = [&](int it, int buf) __attribute__((always_inline)) {
+    load_rows<D, QT, kGeneral, kPairWaves>(qh, sT + (2 * buf + 0) * kTile, it * QT, N, wave, lane);
+    load_rows<D, QT, kGeneral, kPairWaves>(gh, sT + (2 * buf + 1) * kTile, it * QT, N, wave, lane);
+    if (wave == 0) {
+      const int r = min(it * QT + lane, N - 1);
+      dma4(lh + r, sS + (kNStat * buf + 0) * kStat);
+      dma4(dh + r, sS + (kNStat * buf + 1) * kStat);
+      if constexpr (kSeg) dma4(segb + r, sS + (kNStat * buf + 2) * kStat);
+    }
+  };
+  load_tile(it0, 0);
+
+  // Role 0 masks P: the segment id of its lane's key, and whether the pair's
+  // 32 keys share one id.
+  const int seg_k = kSeg ? segb[min(my_k, N - 1)] : 0;
+  int seg_w = 0;
+  bool keys_one_seg = false;
+  if constexpr (kSeg) {
+    seg_w = wave_min(seg_k);
+    keys_one_seg = seg_w == wave_max(seg_k);
+  }
+  // K (role 0) or V (role 1) of this lane's key: the B operand of the first
+  // product.
+  V8 bop[KS];
+  {
+    const uint16_t* src = (role == 0 ? a.k : a.v) + head_off + (int64_t)min(my_k, N - 1) * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bop[ks] = __builtin_bit_cast(V8, *(const u32x4*)(src + 16 * ks));
+  }
+  f32x16 acc[DB];  // role 0: dV^T, role 1: dK^T (rows = head dim, columns = the pair's keys)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  FA2_LDS float* const xp = (FA2_LDS float*)xch_ + (kb * 64 + lane) * 16;
+
+  for (int it = it0; it < it1; ++it) {
+    const int buf = (it - it0) & 1;
+    // Tile it has landed for every wave; every wave is done with the other
+    // buffer and has read the previous tile's P.
+    wait_vm_lds_barrier<0>();
+    if (it + 1 < it1) load_tile(it + 1, buf ^ 1);
+    const FA2_LDS uint16_t* tq = sT + (2 * buf + 0) * kTile;
+    const FA2_LDS uint16_t* tg_ = sT + (2 * buf + 1) * kTile;
+    const FA2_LDS float* tL = sS + (kNStat * buf + 0) * kStat;
+    const FA2_LDS float* tD = sS + (kNStat * buf + 1) * kStat;
+    const FA2_LDS int* tG = (const FA2_LDS int*)(sS + (kNStat * buf + (kSeg ? 2 : 0)) * kStat);
+    const int q0 = it * QT;
+    // (pair-uniform) whether any query of the tile sees a key of this block
+    // (a block wholly past N, in the ragged last key tile, only copies)
+    bool active = kw0 < N && !(kCausal && q0 + 31 < kw0);
+    if constexpr (kGeneral)
+      active = kw0 < N && !(kw0 >= a.prefix && ((a.wr >= 0 && kw0 > q0 + 31 + a.wr) ||
+                                                (a.wl >= 0 && kw0 + 31 < q0 - a.wl)));
+    // LDS operand offsets from lane values formed here, from an opaque lane
+    // index, so that the compiler does not hold them across the loop.
+    const int ln = (int)opaque_vgpr((uint32_t)lane);
+    const int lcol = ln & 31, lhl = (ln >> 5) & 1, ltg = (ln >> 4) & 3, ltl = ln & 15;
+    const uint32_t hz16 = (uint32_t)((lhl ^ swz<D>(lcol)) << 4);
+    f32x16 x = f32x16{};  // role 0: S, role 1: dP (32 queries x 32 keys)
+    uint32_t pk[2][4];    // role 0: P, role 1: dS, packed per 16-query k-step
+    if (active) {
+      const FA2_LDS char* t1 = (const FA2_LDS char*)(role == 0 ? tq : tg_);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t off = (uint32_t)(lcol * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
+        x = E::mfma(__builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(t1 + off)), bop[ks], x);
+      }
+      if (role == 0) {
+        // Element e is query q0 + 8*(e/4) + 4*hl + e%4 of this lane's key.
+        bool need_mask = (q0 + 32 > N) || (kCausal && kw0 + 31 > q0);
+        if constexpr (kGeneral) {
+          bool full = q0 + 31 < N && kw0 + 31 < N &&
+                      (kw0 + 31 < a.prefix ||
+                       ((a.wl < 0 || kw0 >= q0 + 31 - a.wl) && (a.wr < 0 || kw0 + 31 <= q0 + a.wr)));
+          if constexpr (kSeg) {
+            if (full) full = keys_one_seg && __all(tG[col] == seg_w);
+          }
+          need_mask = !full;
+        }
+        const int lim_n = N - q0 - 4 * hl;     // query < N     <=> qi < lim_n
+        const int lim_c = my_k - q0 - 4 * hl;  // key <= query  <=> qi >= lim_c
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 lw = *(const FA2_LDS u32x4*)(tL + 8 * g + 4 * hl);
+          u32x4 sq = {0u, 0u, 0u, 0u};
+          if constexpr (kSeg) sq = *(const FA2_LDS u32x4*)(tG + 8 * g + 4 * hl);
+          float p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * g + i;
+            float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], a.c2, -__uint_as_float(lw[i]) * kLog2e));
+            if (need_mask) {
+              const int qi = 8 * g + i;
+              bool ok = qi < lim_n && (!kCausal || qi >= lim_c);
+              if constexpr (kGeneral) {
+                const int qa = q0 + 4 * hl + qi;
+                ok = ok && (my_k < a.prefix || ((a.wl < 0 || my_k >= qa - a.wl) && (a.wr < 0 || my_k <= qa + a.wr)));
+                if constexpr (kSeg) ok = ok && (int)sq[i] == seg_k;
+              }
+              v = ok ? v : 0.f;
+            }
+            p[i] = v;
+          }
+          *(FA2_LDS u32x4*)(xp + 4 * g) =
+              u32x4{__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3])};
+          pk[g >> 1][2 * (g & 1) + 0] = E::pack2(p[0], p[1]);
+          pk[g >> 1][2 * (g & 1) + 1] = E::pack2(p[2], p[3]);
+        }
+      }
+    }
+    // Role 0's P is visible to role 1.
+    lds_done_barrier();
+    if (active) {
+      if (role == 1) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 p = *(const FA2_LDS u32x4*)(xp + 4 * g);
+          const u32x4 dw = *(const FA2_LDS u32x4*)(tD + 8 * g + 4 * hl);
+          float ds[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ds[i] = __uint_as_float(p[i]) * (x[4 * g + i] - __uint_as_float(dw[i]));
+          pk[g >> 1][2 * (g & 1) + 0] = E::pack2(ds[0], ds[1]);
+          pk[g >> 1][2 * (g & 1) + 1] = E::pack2(ds[2], ds[3]);
+        }
+      }
+      // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1) over the two
+      // 16-query k-steps; the A operand is read transposed, its query rows in
+      // the order the accumulator of the first product holds them.
+      const FA2_LDS char* t2 = (const FA2_LDS char*)(role == 0 ? tg_ : tq);
+      const int x0 = 2 * (ltg & 1) + ((ltl & 3) >> 1);
+      const int x1 = 4 * (ltg >> 1) + (ltl >> 2);
+      const uint32_t w1_16 = (uint32_t)((x0 ^ swz<D>(x1)) << 4), w2_16 = (uint32_t)((x0 ^ swz<D>(x1 + 8)) << 4);
+      const uint32_t t1o = (uint32_t)(x1 * D * 2 + 8 * (ltl & 1));
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const V8 bp = __builtin_bit_cast(V8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
+        const uint32_t rb = (uint32_t)(16 * c * D * 2) + t1o;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint32_t o1 = rb + ((uint32_t)(64 * db) ^ w1_16);
+          const uint32_t o2 = rb + (uint32_t)(8 * D * 2) + ((uint32_t)(64 * db) ^ w2_16);
+          const u32x2 r1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(t2 + o1)));
+          const u32x2 r2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(t2 + o2)));
+          acc[db] = E::mfma(__builtin_bit_cast(V8, u32x4{r1[0], r1[1], r2[0], r2[1]}), bp, acc[db]);
+        }
+      }
+    }
+  }
+  // No LDS write may still be in flight when the workgroup retires.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Element e of block db is head dim 32*db + 8*(e/4) + 4*hl + e%4 of key my_k.
+  if (my_k < N) {
+    uint16_t* dst = (role == 0 ? a.dv : a.dk) + head_off + (int64_t)my_k * D;
+    const float mul = role == 0 ? 1.f : a.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = 32 * db + 8 * r4 + 4 * hl;
+        *(u32x2*)(dst + dim) = u32x2{E::pack2(acc[db][4 * r4 + 0] * mul, acc[db][4 * r4 + 1] * mul),
+                                     E::pack2(acc[db][4 * r4 + 2] * mul, acc[db][4 * r4 + 3] * mul)};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ of kRowsPerWg query rows of one head (d = 64, 128); key/value tiles
+// stream through LDS.
 template <int kDType, int D, int kMask>
-__global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq(BwdArgs a) {
   constexpr bool kCausal = kMask == kMaskCausal;
   constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
   constexpr bool kSeg = kMask == kMaskSegments;
@@ -496,9 +736,8 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
   typedef typename E::V8 V8;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  // Keys per streamed tile: 32 at d = 256, where halving the score and dP
-  // accumulators (and the LDS) takes dQ's spills from 104 to ~70 registers.
-  constexpr int KT = D == 256 ? 32 : kKTile;
+  static_assert(D == 64 || D == 128, "head dim 256: fa2_bwd_dq_pair");
+  constexpr int KT = kKTile;  // keys per streamed tile
   constexpr int kTile = KT * D;
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];  // [buffer][K | V]
@@ -688,6 +927,238 @@ __global__ __launch_bounds__(kThreads, kDqWgPerCu<D>) void fa2_bwd_dq(BwdArgs a)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (my_q < N) {
+    uint16_t* qp = a.dq + head_off + (int64_t)my_q * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = 32 * db + 8 * r4 + 4 * hl;
+        *(u32x2*)(qp + dim) = u32x2{E::pack2(dqt[db][4 * r4 + 0] * a.scale, dqt[db][4 * r4 + 1] * a.scale),
+                                    E::pack2(dqt[db][4 * r4 + 2] * a.scale, dqt[db][4 * r4 + 3] * a.scale)};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ at head dim 256.  The dQ accumulators of 32 rows (128 registers) and the
+// Q and dO operands of those rows (64 each) do not fit one wavefront's share
+// of a SIMD shared with a second wavefront, so two wavefronts share each block
+// of 32 query rows:
+//  * wave rb (role 0) holds Q of the rows, forms S^T = K Q^T and the
+//    probabilities P = exp(s - L), and passes P (fp32) through LDS;
+//  * wave rb + 4 (role 1) holds dO, forms dP^T = V dO^T, then dS = P o (dP - D)
+//    and accumulates dQ^T += K^T dS^T.
+// Eight wavefronts, two per SIMD; every product and rounding as in fa2_bwd_dq.
+template <int kDType, int kMask>
+__global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
+  constexpr int D = 256;
+  constexpr bool kCausal = kMask == kMaskCausal;
+  constexpr bool kGeneral = kMask == kMaskGeneral || kMask == kMaskSegments;
+  constexpr bool kSeg = kMask == kMaskSegments;
+  typedef Elem<kDType> E;
+  typedef typename E::V8 V8;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int KT = 32;  // keys per streamed tile
+  constexpr int kTile = KT * D;
+  static_assert(kRowsPerWg == 4 * 32, "four row blocks per workgroup");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t smem_[2 * 2 * kTile];  // [buffer][K | V]
+  __shared__ __attribute__((aligned(1024))) float xch_[4 * 64 * 16];       // P of each row block, per lane
+  __shared__ __attribute__((aligned(16))) int segk_[kSeg ? 2 * 64 : 4];    // [buffer] the keys' segment ids
+  __shared__ int red_[2 * kPairWaves];                                     // segment span reduction
+  FA2_LDS uint16_t* const sT = (FA2_LDS uint16_t*)smem_;
+
+  const int N = a.N;
+  const int level = blockIdx.x / a.BH;
+  const int bh = blockIdx.x - level * a.BH;
+  const int qt = kCausal ? a.n_q_wg - 1 - level : level;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = wave & 3;     // row block
+  const int role = wave >> 2;  // 0: S, P; 1: dP, dS, dQ
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int col = lane & 31;
+  const int q_row0 = qt * kRowsPerWg + rb * 32;
+  const int my_q = q_row0 + col;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const uint16_t* __restrict__ kh = a.k + head_off;
+  const uint16_t* __restrict__ vh = a.v + head_off;
+  const int* __restrict__ segb = kSeg ? a.seg + (int64_t)(bh / a.H) * N : nullptr;
+
+  // Key tiles visited (as in fa2_bwd_dq).
+  int nt, run_a0 = 0, run_na = 0, run_b0 = 0;
+  if constexpr (kGeneral) {
+    const int q0 = qt * kRowsPerWg, q1 = min(N, q0 + kRowsPerWg) - 1;
+    FwdArgs m{};
+    m.N = N;
+    m.wl = a.wl;
+    m.wr = a.wr;
+    m.prefix = a.prefix;
+    int kf = 0, kl = N - 1;
+    if constexpr (kSeg) {
+      const TileRuns all = general_runs(m, q0, q1, 0, N - 1, KT);
+      const int lo = all.na > 0 ? 0 : all.b0 * KT;
+      const int hi = min(N - 1, (all.b0 + all.nb) * KT - 1);
+      segment_span<kPairWaves>(segb, q0, q1, lo, hi, (FA2_LDS int*)red_, kf, kl);
+    }
+    const TileRuns r = general_runs(m, q0, q1, kf, kl, KT);
+    run_a0 = r.a0;
+    run_na = r.na;
+    run_b0 = r.b0;
+    nt = r.na + r.nb;
+  } else {
+    const int kv_end = kCausal ? min(N, (qt + 1) * kRowsPerWg) : N;
+    nt = (kv_end + KT - 1) / KT;
+  }
+  auto tile_of = [&](int j) __attribute__((always_inline)) {
+    if constexpr (kGeneral) return j < run_na ? run_a0 + j : run_b0 + (j - run_na);
+    else return j;
+  };
+
+  auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
+    const int kv0 = tile_of(j) * KT;
+    load_rows<D, KT, kGeneral, kPairWaves>(kh, sT + (2 * buf + 0) * kTile, kv0, N, wave, lane);
+    load_rows<D, KT, kGeneral, kPairWaves>(vh, sT + (2 * buf + 1) * kTile, kv0, N, wave, lane);
+    if (kSeg && wave == 0) dma4(segb + min(kv0 + lane, N - 1), (FA2_LDS int*)segk_ + buf * 64);
+  };
+  load_tile(0, 0);
+
+  // Q (role 0) or dO (role 1) of this lane's query row: the B operand of the
+  // first product; L (log2 units) and D of the row.
+  const int rq = min(my_q, N - 1);
+  V8 bop[KS];
+  {
+    const uint16_t* src = (role == 0 ? a.q : a.dout) + head_off + (int64_t)rq * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bop[ks] = __builtin_bit_cast(V8, *(const u32x4*)(src + 16 * ks));
+  }
+  const float l2 = a.lse[(int64_t)bh * N + rq] * kLog2e;
+  const float dd = a.delta[(int64_t)bh * N + rq];
+  const int seg_q = kSeg ? segb[rq] : 0;
+  int seg_w = 0;
+  bool rows_one_seg = false;  // the block's 32 rows share one segment id
+  if constexpr (kSeg) {
+    seg_w = wave_min(seg_q);
+    rows_one_seg = seg_w == wave_max(seg_q);
+  }
+
+  f32x16 dqt[DB];  // role 1: dQ^T (rows = head dim, columns = the block's queries)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
+  FA2_LDS uint32_t* const xp = (FA2_LDS uint32_t*)xch_ + (rb * 64 + lane) * 16;
+
+  for (int j = 0; j < nt; ++j) {
+    const int buf = j & 1;
+    // Tile j has landed for every wave; every wave is done with the other
+    // buffer and has read the previous tile's P.
+    wait_vm_lds_barrier<0>();
+    if (j + 1 < nt) load_tile(j + 1, buf ^ 1);
+    const int kv0 = tile_of(j) * KT;
+    // (pair-uniform) whether a row of the block sees a key of the tile (a
+    // block wholly past N, in the ragged last query tile, only copies)
+    bool active = q_row0 < N && (!kCausal || kv0 <= q_row0 + 31);
+    if constexpr (kGeneral)
+      active = q_row0 < N && !(kv0 >= a.prefix && ((a.wr >= 0 && kv0 > q_row0 + 31 + a.wr) ||
+                                                   (a.wl >= 0 && kv0 + KT - 1 < q_row0 - a.wl)));
+    const FA2_LDS uint16_t* tk = sT + (2 * buf + 0) * kTile;
+    const FA2_LDS uint16_t* tv = sT + (2 * buf + 1) * kTile;
+    // LDS operand offsets from lane values formed here, from an opaque lane
+    // index, so that the compiler does not hold them across the loop (as in
+    // fa2_bwd_dkdv at d = 128).
+    const int ln = (int)opaque_vgpr((uint32_t)lane);
+    const int lcol = ln & 31, lhl = (ln >> 5) & 1, ltg = (ln >> 4) & 3, ltl = ln & 15;
+    f32x16 x = f32x16{};  // role 0: S^T, role 1: dP^T (KT keys x 32 queries)
+    if (active) {
+      const FA2_LDS char* t1 = (const FA2_LDS char*)(role == 0 ? tk : tv);
+      const uint32_t hz16 = (uint32_t)((lhl ^ swz<D>(lcol)) << 4);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t off = (uint32_t)(lcol * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
+        x = E::mfma(__builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(t1 + off)), bop[ks], x);
+      }
+      if (role == 0) {
+        // Element e is key kv0 + 8*(e/4) + 4*hl + e%4 of query my_q.
+        const FA2_LDS int* tsg = (const FA2_LDS int*)segk_ + buf * 64;
+        bool need_mask = (kv0 + KT > N) || (kCausal && kv0 + KT - 1 > q_row0);
+        if constexpr (kGeneral) {
+          bool full = kv0 + KT <= N && (kv0 + KT - 1 < a.prefix || ((a.wl < 0 || kv0 >= q_row0 + 31 - a.wl) &&
+                                                                    (a.wr < 0 || kv0 + KT - 1 <= q_row0 + a.wr)));
+          if constexpr (kSeg) {
+            if (full) full = rows_one_seg && __all(tsg[lane % KT] == seg_w);
+          }
+          need_mask = !full;
+        }
+        const int base = kv0 + 4 * hl;
+        float p[16];
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          u32x2 sk = {0u, 0u};
+          if constexpr (kSeg) sk = *(const FA2_LDS u32x2*)(tsg + 8 * (e >> 2) + 4 * hl + (e & 3));
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + i], a.c2, -l2));
+            if (need_mask) {
+              const int key = base + 8 * ((e + i) >> 2) + ((e + i) & 3);
+              bool ok = key < N && (!kCausal || key <= my_q);
+              if constexpr (kGeneral) {
+                ok = ok && (key < a.prefix || ((a.wl < 0 || key >= my_q - a.wl) && (a.wr < 0 || key <= my_q + a.wr)));
+                if constexpr (kSeg) ok = ok && (int)sk[i] == seg_q;
+              }
+              v = ok ? v : 0.f;
+            }
+            p[e + i] = v;
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(FA2_LDS u32x4*)(xp + 4 * g) = u32x4{__float_as_uint(p[4 * g + 0]), __float_as_uint(p[4 * g + 1]),
+                                                __float_as_uint(p[4 * g + 2]), __float_as_uint(p[4 * g + 3])};
+      }
+    }
+    // Role 0's P is visible to role 1.
+    lds_done_barrier();
+    if (active && role == 1) {
+      uint32_t pd[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 p = *(const FA2_LDS u32x4*)(xp + 4 * g);
+        float ds[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ds[i] = __uint_as_float(p[i]) * (x[4 * g + i] - dd);
+        pd[2 * g + 0] = E::pack2(ds[0], ds[1]);
+        pd[2 * g + 1] = E::pack2(ds[2], ds[3]);
+      }
+      // dQ^T += K^T dS^T over the two 16-key k-steps; K^T is read transposed,
+      // rows 16 c + x1 and + 8 (the swizzle of a row depends on its low 4
+      // bits), 4 head dims from 32 db + 4 x0.
+      const int x0 = 2 * (ltg & 1) + ((ltl & 3) >> 1);
+      const int x1 = 4 * (ltg >> 1) + (ltl >> 2);
+      const uint32_t w1_16 = (uint32_t)((x0 ^ swz<D>(x1)) << 4), w2_16 = (uint32_t)((x0 ^ swz<D>(x1 + 8)) << 4);
+      const uint32_t t1o = (uint32_t)(x1 * D * 2 + 8 * (ltl & 1));
+#pragma unroll
+      for (int c = 0; c < KT / 16; ++c) {
+        const V8 bd = __builtin_bit_cast(V8, u32x4{pd[4 * c + 0], pd[4 * c + 1], pd[4 * c + 2], pd[4 * c + 3]});
+        const uint32_t rbase = (uint32_t)(16 * c * D * 2) + t1o;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint32_t o1 = rbase + ((uint32_t)(64 * db) ^ w1_16);
+          const uint32_t o2 = rbase + (uint32_t)(8 * D * 2) + ((uint32_t)(64 * db) ^ w2_16);
+          const u32x2 k1 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tk + o1)));
+          const u32x2 k2 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tk + o2)));
+          dqt[db] = E::mfma(__builtin_bit_cast(V8, u32x4{k1[0], k1[1], k2[0], k2[1]}), bd, dqt[db]);
+        }
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (role == 1 && my_q < N) {
     uint16_t* qp = a.dq + head_off + (int64_t)my_q * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

@@ -45,6 +45,8 @@
 //    operands) and the transposed reads free of bank conflicts.
 #pragma once
 
+#include <type_traits>
+
 #include "fa2_common.h"
 
 namespace fa2 {
@@ -154,15 +156,17 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2
   // instead of being kept (or spilled) across the caller's loop.  (At d = 64
   // the kernels have registers to spare and keep them.)
   const int ln = D >= 128 ? (int)opaque_vgpr((uint32_t)lane) : lane;
-  if (D == 128 && last >= R - 1) {
-    // Whole tile at d = 128: copy t reads 16 * t rows further on and the
-    // swizzle repeats every 16 rows, so one lane offset serves every copy and
-    // the row step goes in the scalar base.  (Measured slower at d = 64 and
-    // 256, where the kernels keep the per-copy offsets below.)
-    static_assert(D != 128 || kStride == 16, "row step of the whole-tile copies");
-    const int s0 = wave * 64 + ln;
-    const int row = s0 / CPR;
-    const uint32_t off = (uint32_t)(row * D * 2 + (((s0 % CPR) ^ swz<D>(row)) << 4));
+  // Whole tile at d = 128, and at d = 256 over eight wavefronts: copy t reads
+  // 16 * t rows further on and the swizzle repeats every 16 rows, so one lane
+  // offset serves every copy and the row step goes in the scalar base.
+  // (Measured slower at d = 64 and in the four-wavefront kernels at d = 256,
+  // which keep the per-copy offsets below.)
+  constexpr bool kOneOffset = D == 128 || (D == 256 && kNW == 8);
+  if (kOneOffset && last >= R - 1) {
+    static_assert(!kOneOffset || kStride == 16, "row step of the whole-tile copies");
+    const uint32_t s0 = (uint32_t)(wave * 64 + ln);
+    const uint32_t row = s0 / CPR;
+    const uint32_t off = row * D * 2 + (((s0 % CPR) ^ (uint32_t)swz<D>((int)row)) << 4);
 #pragma unroll
     for (int t = 0; t < kPer; ++t) dma16_sbase(base + t * kStride * D, off, dst + (t * kNW + wave) * 64 * 8);
     return;
@@ -170,10 +174,10 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ head, FA2
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     const int s0 = (t * kNW + wave) * 64;
-    const int s = s0 + ln;
-    const int row = s / CPR;
-    const int ch = (s % CPR) ^ swz<D>(row);
-    dma16_sbase(base, (uint32_t)(min(row, last) * D * 2 + ch * 16), dst + s0 * 8);
+    const uint32_t s = (uint32_t)(s0 + ln);
+    const uint32_t row = s / CPR;
+    const uint32_t ch = (s % CPR) ^ (uint32_t)swz<D>((int)row);
+    dma16_sbase(base, (uint32_t)min((int)row, last) * D * 2 + ch * 16, dst + s0 * 8);
   }
 }
 
@@ -494,6 +498,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dkdv(BwdArgs a) {
 // single-wavefront kernel performs, in the same order.
 constexpr int kPairWaves = 8;
 constexpr int kPairThreads = 64 * kPairWaves;
+// LDS operand fragments read ahead of their products (two under segment ids,
+// whose mask state leaves fewer registers).
+template <int kMask> constexpr int kPairPipe = kMask == kMaskSegments ? 2 : 4;
 
 template <int kDType, int kMask>
 __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) {
@@ -587,10 +594,18 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) bop[ks] = __builtin_bit_cast(V8, *(const u32x4*)(src + 16 * ks));
   }
+  // The compiler waits for these loads here, once: otherwise it waits for them
+  // inside the loop, and that wait (a count of outstanding loads) also waits
+  // for the next tile's copies, which the hardware counts alike.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(bop[ks]));
   f32x16 acc[DB];  // role 0: dV^T, role 1: dK^T (rows = head dim, columns = the pair's keys)
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  FA2_LDS float* const xp = (FA2_LDS float*)xch_ + (kb * 64 + lane) * 16;
+  // P of the pair's block: quarter g (4 values per lane) at ((kb * 4 + g) * 64 +
+  // lane) * 4 floats, so that each 16-byte store and load of a wave covers
+  // 1 KB of consecutive slots (no bank conflicts).
+  FA2_LDS float* const xp = (FA2_LDS float*)xch_ + (kb * 4 * 64 + lane) * 4;
 
   for (int it = it0; it < it1; ++it) {
     const int buf = (it - it0) & 1;
@@ -619,11 +634,21 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
     uint32_t pk[2][4];    // role 0: P, role 1: dS, packed per 16-query k-step
     if (active) {
       const FA2_LDS char* t1 = (const FA2_LDS char*)(role == 0 ? tq : tg_);
+      auto row_frag = [&](int ks) __attribute__((always_inline)) {
+        const uint32_t off = (uint32_t)(lcol * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
+        return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(t1 + off));
+      };
+      // Operand reads kPairPipe fragments ahead of their products.
+      V8 fr[kPairPipe<kMask>];
+#pragma unroll
+      for (int u = 0; u < kPairPipe<kMask>; ++u) fr[u] = row_frag(u);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t off = (uint32_t)(lcol * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
-        x = E::mfma(__builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(t1 + off)), bop[ks], x);
+        __builtin_amdgcn_sched_barrier(0);
+        x = E::mfma(fr[ks % kPairPipe<kMask>], bop[ks], x);
+        if (ks + kPairPipe<kMask> < KS) fr[ks % kPairPipe<kMask>] = row_frag(ks + kPairPipe<kMask>);
       }
+      __builtin_amdgcn_sched_barrier(0);
       if (role == 0) {
         // Element e is query q0 + 8*(e/4) + 4*hl + e%4 of this lane's key.
         bool need_mask = (q0 + 32 > N) || (kCausal && kw0 + 31 > q0);
@@ -638,33 +663,41 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
         }
         const int lim_n = N - q0 - 4 * hl;     // query < N     <=> qi < lim_n
         const int lim_c = my_k - q0 - 4 * hl;  // key <= query  <=> qi >= lim_c
+        // The masked and the unmasked variant as separate branches: one
+        // variant with the mask behind a select would evaluate the mask on
+        // every tile.
+        auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x4 lw = *(const FA2_LDS u32x4*)(tL + 8 * g + 4 * hl);
-          u32x4 sq = {0u, 0u, 0u, 0u};
-          if constexpr (kSeg) sq = *(const FA2_LDS u32x4*)(tG + 8 * g + 4 * hl);
-          float p[4];
+          for (int g = 0; g < 4; ++g) {
+            const u32x4 lw = *(const FA2_LDS u32x4*)(tL + 8 * g + 4 * hl);
+            u32x4 sq = {0u, 0u, 0u, 0u};
+            if constexpr (kSeg && decltype(masked)::value) sq = *(const FA2_LDS u32x4*)(tG + 8 * g + 4 * hl);
+            float p[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = 4 * g + i;
-            float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], a.c2, -__uint_as_float(lw[i]) * kLog2e));
-            if (need_mask) {
-              const int qi = 8 * g + i;
-              bool ok = qi < lim_n && (!kCausal || qi >= lim_c);
-              if constexpr (kGeneral) {
-                const int qa = q0 + 4 * hl + qi;
-                ok = ok && (my_k < a.prefix || ((a.wl < 0 || my_k >= qa - a.wl) && (a.wr < 0 || my_k <= qa + a.wr)));
-                if constexpr (kSeg) ok = ok && (int)sq[i] == seg_k;
+            for (int i = 0; i < 4; ++i) {
+              const int e = 4 * g + i;
+              float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], a.c2, -__uint_as_float(lw[i]) * kLog2e));
+              if constexpr (decltype(masked)::value) {
+                const int qi = 8 * g + i;
+                bool ok = qi < lim_n && (!kCausal || qi >= lim_c);
+                if constexpr (kGeneral) {
+                  const int qa = q0 + 4 * hl + qi;
+                  ok = ok &&
+                       (my_k < a.prefix || ((a.wl < 0 || my_k >= qa - a.wl) && (a.wr < 0 || my_k <= qa + a.wr)));
+                  if constexpr (kSeg) ok = ok && (int)sq[i] == seg_k;
+                }
+                v = ok ? v : 0.f;
               }
-              v = ok ? v : 0.f;
+              p[i] = v;
             }
-            p[i] = v;
+            *(FA2_LDS u32x4*)(xp + 256 * g) =
+                u32x4{__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3])};
+            pk[g >> 1][2 * (g & 1) + 0] = E::pack2(p[0], p[1]);
+            pk[g >> 1][2 * (g & 1) + 1] = E::pack2(p[2], p[3]);
           }
-          *(FA2_LDS u32x4*)(xp + 4 * g) =
-              u32x4{__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3])};
-          pk[g >> 1][2 * (g & 1) + 0] = E::pack2(p[0], p[1]);
-          pk[g >> 1][2 * (g & 1) + 1] = E::pack2(p[2], p[3]);
-        }
+        };
+        if (need_mask) probs(std::true_type{});
+        else probs(std::false_type{});
       }
     }
     // Role 0's P is visible to role 1.
@@ -673,7 +706,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
       if (role == 1) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const u32x4 p = *(const FA2_LDS u32x4*)(xp + 4 * g);
+          const u32x4 p = *(const FA2_LDS u32x4*)(xp + 256 * g);
           const u32x4 dw = *(const FA2_LDS u32x4*)(tD + 8 * g + 4 * hl);
           float ds[4];
 #pragma unroll
@@ -690,19 +723,27 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
       const int x1 = 4 * (ltg >> 1) + (ltl >> 2);
       const uint32_t w1_16 = (uint32_t)((x0 ^ swz<D>(x1)) << 4), w2_16 = (uint32_t)((x0 ^ swz<D>(x1 + 8)) << 4);
       const uint32_t t1o = (uint32_t)(x1 * D * 2 + 8 * (ltl & 1));
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const V8 bp = __builtin_bit_cast(V8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
+      auto tr_frag = [&](int u) __attribute__((always_inline)) {  // fragment u = (c, db)
+        const int c = u / DB, db = u % DB;
         const uint32_t rb = (uint32_t)(16 * c * D * 2) + t1o;
+        const uint32_t o1 = rb + ((uint32_t)(64 * db) ^ w1_16);
+        const uint32_t o2 = rb + (uint32_t)(8 * D * 2) + ((uint32_t)(64 * db) ^ w2_16);
+        const u32x2 r1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(t2 + o1)));
+        const u32x2 r2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(t2 + o2)));
+        return __builtin_bit_cast(V8, u32x4{r1[0], r1[1], r2[0], r2[1]});
+      };
+      V8 fr[kPairPipe<kMask>];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint32_t o1 = rb + ((uint32_t)(64 * db) ^ w1_16);
-          const uint32_t o2 = rb + (uint32_t)(8 * D * 2) + ((uint32_t)(64 * db) ^ w2_16);
-          const u32x2 r1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(t2 + o1)));
-          const u32x2 r2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)(t2 + o2)));
-          acc[db] = E::mfma(__builtin_bit_cast(V8, u32x4{r1[0], r1[1], r2[0], r2[1]}), bp, acc[db]);
-        }
+      for (int u = 0; u < kPairPipe<kMask>; ++u) fr[u] = tr_frag(u);
+#pragma unroll
+      for (int u = 0; u < 2 * DB; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int c = u / DB, db = u % DB;
+        const V8 bp = __builtin_bit_cast(V8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
+        acc[db] = E::mfma(fr[u % kPairPipe<kMask>], bp, acc[db]);
+        if (u + kPairPipe<kMask> < 2 * DB) fr[u % kPairPipe<kMask>] = tr_frag(u + kPairPipe<kMask>);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // No LDS write may still be in flight when the workgroup retires.
@@ -1036,8 +1077,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) bop[ks] = __builtin_bit_cast(V8, *(const u32x4*)(src + 16 * ks));
   }
-  const float l2 = a.lse[(int64_t)bh * N + rq] * kLog2e;
-  const float dd = a.delta[(int64_t)bh * N + rq];
+  float l2 = a.lse[(int64_t)bh * N + rq] * kLog2e;
+  float dd = a.delta[(int64_t)bh * N + rq];
   const int seg_q = kSeg ? segb[rq] : 0;
   int seg_w = 0;
   bool rows_one_seg = false;  // the block's 32 rows share one segment id
@@ -1045,11 +1086,17 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
     seg_w = wave_min(seg_q);
     rows_one_seg = seg_w == wave_max(seg_q);
   }
+  // The compiler waits for these loads here, once (see fa2_bwd_dkdv_pair).
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(bop[ks]));
+  asm volatile("" : "+v"(l2), "+v"(dd));
 
   f32x16 dqt[DB];  // role 1: dQ^T (rows = head dim, columns = the block's queries)
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
-  FA2_LDS uint32_t* const xp = (FA2_LDS uint32_t*)xch_ + (rb * 64 + lane) * 16;
+  // P of the block: quarter g at ((rb * 4 + g) * 64 + lane) * 4 words (each
+  // 16-byte store and load of a wave covers 1 KB of consecutive slots).
+  FA2_LDS uint32_t* const xp = (FA2_LDS uint32_t*)xch_ + (rb * 4 * 64 + lane) * 4;
 
   for (int j = 0; j < nt; ++j) {
     const int buf = j & 1;
@@ -1075,11 +1122,20 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
     if (active) {
       const FA2_LDS char* t1 = (const FA2_LDS char*)(role == 0 ? tk : tv);
       const uint32_t hz16 = (uint32_t)((lhl ^ swz<D>(lcol)) << 4);
+      auto row_frag = [&](int ks) __attribute__((always_inline)) {
+        const uint32_t off = (uint32_t)(lcol * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
+        return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(t1 + off));
+      };
+      V8 fr[kPairPipe<kMask>];
+#pragma unroll
+      for (int u = 0; u < kPairPipe<kMask>; ++u) fr[u] = row_frag(u);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t off = (uint32_t)(lcol * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
-        x = E::mfma(__builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(t1 + off)), bop[ks], x);
+        __builtin_amdgcn_sched_barrier(0);
+        x = E::mfma(fr[ks % kPairPipe<kMask>], bop[ks], x);
+        if (ks + kPairPipe<kMask> < KS) fr[ks % kPairPipe<kMask>] = row_frag(ks + kPairPipe<kMask>);
       }
+      __builtin_amdgcn_sched_barrier(0);
       if (role == 0) {
         // Element e is key kv0 + 8*(e/4) + 4*hl + e%4 of query my_q.
         const FA2_LDS int* tsg = (const FA2_LDS int*)segk_ + buf * 64;
@@ -1093,30 +1149,38 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
           need_mask = !full;
         }
         const int base = kv0 + 4 * hl;
-        float p[16];
+        // Masked and unmasked variants as separate branches (see
+        // fa2_bwd_dkdv_pair).
+        auto probs = [&](auto masked) __attribute__((always_inline)) {
+          float p[16];
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          u32x2 sk = {0u, 0u};
-          if constexpr (kSeg) sk = *(const FA2_LDS u32x2*)(tsg + 8 * (e >> 2) + 4 * hl + (e & 3));
+          for (int e = 0; e < 16; e += 2) {
+            u32x2 sk = {0u, 0u};
+            if constexpr (kSeg && decltype(masked)::value)
+              sk = *(const FA2_LDS u32x2*)(tsg + 8 * (e >> 2) + 4 * hl + (e & 3));
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + i], a.c2, -l2));
-            if (need_mask) {
-              const int key = base + 8 * ((e + i) >> 2) + ((e + i) & 3);
-              bool ok = key < N && (!kCausal || key <= my_q);
-              if constexpr (kGeneral) {
-                ok = ok && (key < a.prefix || ((a.wl < 0 || key >= my_q - a.wl) && (a.wr < 0 || key <= my_q + a.wr)));
-                if constexpr (kSeg) ok = ok && (int)sk[i] == seg_q;
+            for (int i = 0; i < 2; ++i) {
+              float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + i], a.c2, -l2));
+              if constexpr (decltype(masked)::value) {
+                const int key = base + 8 * ((e + i) >> 2) + ((e + i) & 3);
+                bool ok = key < N && (!kCausal || key <= my_q);
+                if constexpr (kGeneral) {
+                  ok = ok &&
+                       (key < a.prefix || ((a.wl < 0 || key >= my_q - a.wl) && (a.wr < 0 || key <= my_q + a.wr)));
+                  if constexpr (kSeg) ok = ok && (int)sk[i] == seg_q;
+                }
+                v = ok ? v : 0.f;
               }
-              v = ok ? v : 0.f;
+              p[e + i] = v;
             }
-            p[e + i] = v;
           }
-        }
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *(FA2_LDS u32x4*)(xp + 4 * g) = u32x4{__float_as_uint(p[4 * g + 0]), __float_as_uint(p[4 * g + 1]),
-                                                __float_as_uint(p[4 * g + 2]), __float_as_uint(p[4 * g + 3])};
+          for (int g = 0; g < 4; ++g)
+            *(FA2_LDS u32x4*)(xp + 256 * g) = u32x4{__float_as_uint(p[4 * g + 0]), __float_as_uint(p[4 * g + 1]),
+                                                  __float_as_uint(p[4 * g + 2]), __float_as_uint(p[4 * g + 3])};
+        };
+        if (need_mask) probs(std::true_type{});
+        else probs(std::false_type{});
       }
     }
     // Role 0's P is visible to role 1.
@@ -1125,7 +1189,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
       uint32_t pd[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const u32x4 p = *(const FA2_LDS u32x4*)(xp + 4 * g);
+        const u32x4 p = *(const FA2_LDS u32x4*)(xp + 256 * g);
         float ds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ds[i] = __uint_as_float(p[i]) * (x[4 * g + i] - dd);
@@ -1139,21 +1203,30 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
       const int x1 = 4 * (ltg >> 1) + (ltl >> 2);
       const uint32_t w1_16 = (uint32_t)((x0 ^ swz<D>(x1)) << 4), w2_16 = (uint32_t)((x0 ^ swz<D>(x1 + 8)) << 4);
       const uint32_t t1o = (uint32_t)(x1 * D * 2 + 8 * (ltl & 1));
-#pragma unroll
-      for (int c = 0; c < KT / 16; ++c) {
-        const V8 bd = __builtin_bit_cast(V8, u32x4{pd[4 * c + 0], pd[4 * c + 1], pd[4 * c + 2], pd[4 * c + 3]});
+      auto tr_frag = [&](int u) __attribute__((always_inline)) {  // fragment u = (c, db)
+        const int c = u / DB, db = u % DB;
         const uint32_t rbase = (uint32_t)(16 * c * D * 2) + t1o;
+        const uint32_t o1 = rbase + ((uint32_t)(64 * db) ^ w1_16);
+        const uint32_t o2 = rbase + (uint32_t)(8 * D * 2) + ((uint32_t)(64 * db) ^ w2_16);
+        const u32x2 k1 = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tk + o1)));
+        const u32x2 k2 = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tk + o2)));
+        return __builtin_bit_cast(V8, u32x4{k1[0], k1[1], k2[0], k2[1]});
+      };
+      // Operand reads kPairPipe fragments ahead of their products.
+      V8 fr[kPairPipe<kMask>];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint32_t o1 = rbase + ((uint32_t)(64 * db) ^ w1_16);
-          const uint32_t o2 = rbase + (uint32_t)(8 * D * 2) + ((uint32_t)(64 * db) ^ w2_16);
-          const u32x2 k1 = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tk + o1)));
-          const u32x2 k2 = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)((const FA2_LDS char*)tk + o2)));
-          dqt[db] = E::mfma(__builtin_bit_cast(V8, u32x4{k1[0], k1[1], k2[0], k2[1]}), bd, dqt[db]);
-        }
+      for (int u = 0; u < kPairPipe<kMask>; ++u) fr[u] = tr_frag(u);
+#pragma unroll
+      for (int u = 0; u < (KT / 16) * DB; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int c = u / DB, db = u % DB;
+        const V8 bd = __builtin_bit_cast(V8, u32x4{pd[4 * c + 0], pd[4 * c + 1], pd[4 * c + 2], pd[4 * c + 3]});
+        dqt[db] = E::mfma(fr[u % kPairPipe<kMask>], bd, dqt[db]);
+        if (u + kPairPipe<kMask> < (KT / 16) * DB) fr[u % kPairPipe<kMask>] = tr_frag(u + kPairPipe<kMask>);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

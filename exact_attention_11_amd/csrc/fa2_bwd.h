@@ -318,6 +318,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dkdv(BwdArgs a) {
       vf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(vp + 16 * ks));
     }
   }
+  // The compiler waits for these loads here, once: otherwise it waits for them
+  // inside the loop, and that wait (a count of outstanding loads) also waits
+  // for the next tile's copies, which the hardware counts alike.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
 
   f32x16 dkt[DB], dvt[DB];  // dK^T, dV^T: rows = head dim, columns = this wave's keys
 #pragma unroll
@@ -594,9 +599,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) bop[ks] = __builtin_bit_cast(V8, *(const u32x4*)(src + 16 * ks));
   }
-  // The compiler waits for these loads here, once: otherwise it waits for them
-  // inside the loop, and that wait (a count of outstanding loads) also waits
-  // for the next tile's copies, which the hardware counts alike.
+  // The compiler waits for these loads here, once (see fa2_bwd_dkdv).
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(bop[ks]));
   f32x16 acc[DB];  // role 0: dV^T, role 1: dK^T (rows = head dim, columns = the pair's keys)
@@ -860,8 +863,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq(BwdArgs a) {
       gf[ks] = __builtin_bit_cast(V8, *(const u32x4*)(gp + 16 * ks));
     }
   }
-  const float l2 = a.lse[(int64_t)bh * N + rq] * kLog2e;
-  const float dd = a.delta[(int64_t)bh * N + rq];
+  float l2 = a.lse[(int64_t)bh * N + rq] * kLog2e;
+  float dd = a.delta[(int64_t)bh * N + rq];
   const int seg_q = kSeg ? segb[rq] : 0;
   int seg_w = 0;
   bool rows_one_seg = false;  // the wave's 32 rows share one segment id
@@ -869,6 +872,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq(BwdArgs a) {
     seg_w = wave_min(seg_q);
     rows_one_seg = seg_w == wave_max(seg_q);
   }
+  // The compiler waits for these loads here, once (see fa2_bwd_dkdv).
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(gf[ks]));
+  asm volatile("" : "+v"(l2), "+v"(dd));
 
   f32x16 dqt[DB];  // dQ^T: rows = head dim, columns = this wave's queries
 #pragma unroll
@@ -1086,7 +1093,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
     seg_w = wave_min(seg_q);
     rows_one_seg = seg_w == wave_max(seg_q);
   }
-  // The compiler waits for these loads here, once (see fa2_bwd_dkdv_pair).
+  // The compiler waits for these loads here, once (see fa2_bwd_dkdv).
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(bop[ks]));
   asm volatile("" : "+v"(l2), "+v"(dd));

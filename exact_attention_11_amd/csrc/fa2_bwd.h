@@ -401,34 +401,47 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dkdv(BwdArgs a) {
       const int lim_n = N - q0 - 4 * hl;          // query < N      <=> qi < lim_n
       const int lim_c = my_k - q0 - 4 * hl;       // key <= query   <=> qi >= lim_c
       uint32_t pp[2][4], pd[2][4];                // P and dS packed, per 16-query k-step
+      // The masked and the unmasked variant as separate branches: one variant
+      // with the mask behind a select would evaluate the mask on every block.
+      auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x4 lw = *(const FA2_LDS u32x4*)(tL + sb * 32 + 8 * g + 4 * hl);
-        const u32x4 dw = *(const FA2_LDS u32x4*)(tD + sb * 32 + 8 * g + 4 * hl);
-        u32x4 sq = {0u, 0u, 0u, 0u};
-        if constexpr (kSeg) sq = *(const FA2_LDS u32x4*)(tG + sb * 32 + 8 * g + 4 * hl);
-        float p[4], ds[4];
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 lw = *(const FA2_LDS u32x4*)(tL + sb * 32 + 8 * g + 4 * hl);
+          const u32x4 dw = *(const FA2_LDS u32x4*)(tD + sb * 32 + 8 * g + 4 * hl);
+          u32x4 sq = {0u, 0u, 0u, 0u};
+          if constexpr (kSeg && decltype(masked)::value) sq = *(const FA2_LDS u32x4*)(tG + sb * 32 + 8 * g + 4 * hl);
+          float p[4], ds[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * g + i;
-          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c2, -__uint_as_float(lw[i]) * kLog2e));
-          if (need_mask) {
-            const int qi = 8 * g + i;
-            bool ok = qi < lim_n && (!kCausal || qi >= lim_c);
-            if constexpr (kGeneral) {
-              const int qa = q0 + 4 * hl + qi;  // the query of this element
-              ok = ok && (my_k < a.prefix || ((a.wl < 0 || my_k >= qa - a.wl) && (a.wr < 0 || my_k <= qa + a.wr)));
-              if constexpr (kSeg) ok = ok && (int)sq[i] == seg_k;
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * g + i;
+            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c2, -__uint_as_float(lw[i]) * kLog2e));
+            if (decltype(masked)::value && (D != 128 || need_mask)) {
+              const int qi = 8 * g + i;
+              bool ok = qi < lim_n && (!kCausal || qi >= lim_c);
+              if constexpr (kGeneral) {
+                const int qa = q0 + 4 * hl + qi;  // the query of this element
+                ok = ok &&
+                     (my_k < a.prefix || ((a.wl < 0 || my_k >= qa - a.wl) && (a.wr < 0 || my_k <= qa + a.wr)));
+                if constexpr (kSeg) ok = ok && (int)sq[i] == seg_k;
+              }
+              x = ok ? x : 0.f;
             }
-            x = ok ? x : 0.f;
+            p[i] = x;
+            ds[i] = x * (dp[e] - __uint_as_float(dw[i]));
           }
-          p[i] = x;
-          ds[i] = x * (dp[e] - __uint_as_float(dw[i]));
+          pp[g >> 1][2 * (g & 1) + 0] = E::pack2(p[0], p[1]);
+          pp[g >> 1][2 * (g & 1) + 1] = E::pack2(p[2], p[3]);
+          pd[g >> 1][2 * (g & 1) + 0] = E::pack2(ds[0], ds[1]);
+          pd[g >> 1][2 * (g & 1) + 1] = E::pack2(ds[2], ds[3]);
         }
-        pp[g >> 1][2 * (g & 1) + 0] = E::pack2(p[0], p[1]);
-        pp[g >> 1][2 * (g & 1) + 1] = E::pack2(p[2], p[3]);
-        pd[g >> 1][2 * (g & 1) + 0] = E::pack2(ds[0], ds[1]);
-        pd[g >> 1][2 * (g & 1) + 1] = E::pack2(ds[2], ds[3]);
+      };
+      if constexpr (D == 128) {
+        // At d = 128 the two variants as separate code exceed the registers
+        // (spills): the mask stays a select, evaluated on every block.
+        probs(std::true_type{});
+      } else {
+        if (need_mask) probs(std::true_type{});
+        else probs(std::false_type{});
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps.
 #pragma unroll
@@ -928,30 +941,37 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq(BwdArgs a) {
     }
     const int base = kv0 + 4 * hl;
     uint32_t pd[KT / 32][8];
+    // Masked and unmasked variants as separate branches (see fa2_bwd_dkdv).
+    auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < KT / 32; ++kb) {
+      for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        float ds2[2];
-        u32x2 sk = {0u, 0u};
-        if constexpr (kSeg) sk = *(const FA2_LDS u32x2*)(tsg + 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3));
+        for (int e = 0; e < 16; e += 2) {
+          float ds2[2];
+          u32x2 sk = {0u, 0u};
+          if constexpr (kSeg && decltype(masked)::value)
+            sk = *(const FA2_LDS u32x2*)(tsg + 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3));
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + i], a.c2, -l2));
-          if (need_mask) {
-            const int key = base + 32 * kb + 8 * ((e + i) >> 2) + ((e + i) & 3);
-            bool ok = key < N && (!kCausal || key <= my_q);
-            if constexpr (kGeneral) {
-              ok = ok && (key < a.prefix || ((a.wl < 0 || key >= my_q - a.wl) && (a.wr < 0 || key <= my_q + a.wr)));
-              if constexpr (kSeg) ok = ok && (int)sk[i] == seg_q;
+          for (int i = 0; i < 2; ++i) {
+            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + i], a.c2, -l2));
+            if constexpr (decltype(masked)::value) {
+              const int key = base + 32 * kb + 8 * ((e + i) >> 2) + ((e + i) & 3);
+              bool ok = key < N && (!kCausal || key <= my_q);
+              if constexpr (kGeneral) {
+                ok = ok &&
+                     (key < a.prefix || ((a.wl < 0 || key >= my_q - a.wl) && (a.wr < 0 || key <= my_q + a.wr)));
+                if constexpr (kSeg) ok = ok && (int)sk[i] == seg_q;
+              }
+              x = ok ? x : 0.f;
             }
-            x = ok ? x : 0.f;
+            ds2[i] = x * (dp[kb][e + i] - dd);
           }
-          ds2[i] = x * (dp[kb][e + i] - dd);
+          pd[kb][e >> 1] = E::pack2(ds2[0], ds2[1]);
         }
-        pd[kb][e >> 1] = E::pack2(ds2[0], ds2[1]);
       }
-    }
+    };
+    if (need_mask) probs(std::true_type{});
+    else probs(std::false_type{});
     // dQ^T += K^T dS^T over the 16-key k-steps.
 #pragma unroll
     for (int c = 0; c < KT / 16; ++c) {

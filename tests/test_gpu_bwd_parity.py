@@ -152,3 +152,35 @@ def test_bwd_on_a_side_stream():
     for got in outs:
         for a, b in zip(got, ref):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["b8h16_n2048_d64", "b8h16_n2048_d128_causal", "b4h8_n4099_d256_peaky",
+                                  "b1h32_n16384_d128_causal"])
+def test_bwd_parity_workload_full_size(name):
+    """A named workload at its full size, in the launch configuration that
+    bench.py's gradient pass times: whole (batch, head) slices against the
+    gradient oracle (the first and the last slice; the last only at 16384
+    rows, where one slice costs the oracle about half a minute), and every
+    output finite."""
+    from exact_attention_11_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[name]
+    dtype = w.torch_dtype
+    q, k, v = workload_inputs(w, seed=0)
+    do = _dout(q.shape, dtype, 0)
+    _log(f"workload {name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
+    o, dq, dk, dv, delta = _run(q, k, v, do, w.causal, w.scale)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all(), name
+    s32 = float(np.float32(w.scale))
+    slices = [(w.B - 1, w.H - 1)] if w.N > 8192 else [(0, 0), (w.B - 1, w.H - 1)]
+    for (b, h) in slices:
+        rq, rk, rv, _ = oracle.attention_bwd_f64(q[b, h].double().numpy(), k[b, h].double().numpy(),
+                                                 v[b, h].double().numpy(), do[b, h].double().numpy(), w.causal, s32)
+        what = f"{name} (b={b},h={h})"
+        _check("dQ", dq[b, h], rq, dtype, what)
+        _check("dK", dk[b, h], rk, dtype, what)
+        _check("dV", dv[b, h], rv, dtype, what)
+    want = (do.double() * o.double()).sum(-1).numpy()
+    err = float(np.max(np.abs(delta.double().numpy() - want)))
+    assert err <= 1e-5 * max(1.0, float(np.max(np.abs(want)))), (name, "D", err)

@@ -623,6 +623,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
   // 1 KB of consecutive slots (no bank conflicts).
   FA2_LDS float* const xp = (FA2_LDS float*)xch_ + (kb * 4 * 64 + lane) * 4;
 
+  // Each role runs its own copy of the query loop (the same barriers in the
+  // same order), so that the compiler sees which registers each keeps live.
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+  constexpr int R = decltype(role_c)::value;
   for (int it = it0; it < it1; ++it) {
     const int buf = (it - it0) & 1;
     // Tile it has landed for every wave; every wave is done with the other
@@ -649,7 +653,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
     f32x16 x = f32x16{};  // role 0: S, role 1: dP (32 queries x 32 keys)
     uint32_t pk[2][4];    // role 0: P, role 1: dS, packed per 16-query k-step
     if (active) {
-      const FA2_LDS char* t1 = (const FA2_LDS char*)(role == 0 ? tq : tg_);
+      const FA2_LDS char* t1 = (const FA2_LDS char*)(R == 0 ? tq : tg_);
       auto row_frag = [&](int ks) __attribute__((always_inline)) {
         const uint32_t off = (uint32_t)(lcol * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
         return __builtin_bit_cast(V8, *(const FA2_LDS u32x4*)(t1 + off));
@@ -665,7 +669,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
         if (ks + kPairPipe<kMask> < KS) fr[ks % kPairPipe<kMask>] = row_frag(ks + kPairPipe<kMask>);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (role == 0) {
+      if constexpr (R == 0) {
         // Element e is query q0 + 8*(e/4) + 4*hl + e%4 of this lane's key.
         bool need_mask = (q0 + 32 > N) || (kCausal && kw0 + 31 > q0);
         if constexpr (kGeneral) {
@@ -719,7 +723,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
     // Role 0's P is visible to role 1.
     lds_done_barrier();
     if (active) {
-      if (role == 1) {
+      if constexpr (R == 1) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const u32x4 p = *(const FA2_LDS u32x4*)(xp + 256 * g);
@@ -734,7 +738,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
       // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1) over the two
       // 16-query k-steps; the A operand is read transposed, its query rows in
       // the order the accumulator of the first product holds them.
-      const FA2_LDS char* t2 = (const FA2_LDS char*)(role == 0 ? tg_ : tq);
+      const FA2_LDS char* t2 = (const FA2_LDS char*)(R == 0 ? tg_ : tq);
       const int x0 = 2 * (ltg & 1) + ((ltl & 3) >> 1);
       const int x1 = 4 * (ltg >> 1) + (ltl >> 2);
       const uint32_t w1_16 = (uint32_t)((x0 ^ swz<D>(x1)) << 4), w2_16 = (uint32_t)((x0 ^ swz<D>(x1 + 8)) << 4);
@@ -762,6 +766,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dkdv_pair(BwdArgs a) 
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  };
+  if (role == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
   // No LDS write may still be in flight when the workgroup retires.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -1118,12 +1125,19 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
   for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(bop[ks]));
   asm volatile("" : "+v"(l2), "+v"(dd));
 
-  f32x16 dqt[DB];  // role 1: dQ^T (rows = head dim, columns = the block's queries)
-#pragma unroll
-  for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
   // P of the block: quarter g at ((rb * 4 + g) * 64 + lane) * 4 words (each
   // 16-byte store and load of a wave covers 1 KB of consecutive slots).
   FA2_LDS uint32_t* const xp = (FA2_LDS uint32_t*)xch_ + (rb * 4 * 64 + lane) * 4;
+
+  // Each role runs its own copy of the key loop (the same barriers in the same
+  // order), so that the compiler sees which registers each keeps live: role 0
+  // holds no dQ accumulators.
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+  constexpr int R = decltype(role_c)::value;
+  constexpr int kDqt = R == 1 ? DB : 1;
+  f32x16 dqt[kDqt];  // role 1: dQ^T (rows = head dim, columns = the block's queries)
+#pragma unroll
+  for (int db = 0; db < kDqt; ++db) dqt[db] = f32x16{};
 
   for (int j = 0; j < nt; ++j) {
     const int buf = j & 1;
@@ -1147,7 +1161,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
     const int lcol = ln & 31, lhl = (ln >> 5) & 1, ltg = (ln >> 4) & 3, ltl = ln & 15;
     f32x16 x = f32x16{};  // role 0: S^T, role 1: dP^T (KT keys x 32 queries)
     if (active) {
-      const FA2_LDS char* t1 = (const FA2_LDS char*)(role == 0 ? tk : tv);
+      const FA2_LDS char* t1 = (const FA2_LDS char*)(R == 0 ? tk : tv);
       const uint32_t hz16 = (uint32_t)((lhl ^ swz<D>(lcol)) << 4);
       auto row_frag = [&](int ks) __attribute__((always_inline)) {
         const uint32_t off = (uint32_t)(lcol * D * 2) + ((uint32_t)(32 * ks) ^ hz16);
@@ -1163,7 +1177,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
         if (ks + kPairPipe<kMask> < KS) fr[ks % kPairPipe<kMask>] = row_frag(ks + kPairPipe<kMask>);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (role == 0) {
+      if constexpr (R == 0) {
         // Element e is key kv0 + 8*(e/4) + 4*hl + e%4 of query my_q.
         const FA2_LDS int* tsg = (const FA2_LDS int*)segk_ + buf * 64;
         bool need_mask = (kv0 + KT > N) || (kCausal && kv0 + KT - 1 > q_row0);
@@ -1212,7 +1226,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
     }
     // Role 0's P is visible to role 1.
     lds_done_barrier();
-    if (active && role == 1) {
+    if (R == 1 && active) {
       uint32_t pd[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -1250,7 +1264,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         const int c = u / DB, db = u % DB;
         const V8 bd = __builtin_bit_cast(V8, u32x4{pd[4 * c + 0], pd[4 * c + 1], pd[4 * c + 2], pd[4 * c + 3]});
-        dqt[db] = E::mfma(fr[u % kPairPipe<kMask>], bd, dqt[db]);
+        dqt[db % kDqt] = E::mfma(fr[u % kPairPipe<kMask>], bd, dqt[db % kDqt]);
         if (u + kPairPipe<kMask> < (KT / 16) * DB) fr[u % kPairPipe<kMask>] = tr_frag(u + kPairPipe<kMask>);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1258,18 +1272,22 @@ __global__ __launch_bounds__(kPairThreads, 1) void fa2_bwd_dq_pair(BwdArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  if (role == 1 && my_q < N) {
+  if (R == 1 && my_q < N) {
     uint16_t* qp = a.dq + head_off + (int64_t)my_q * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int dim = 32 * db + 8 * r4 + 4 * hl;
-        *(u32x2*)(qp + dim) = u32x2{E::pack2(dqt[db][4 * r4 + 0] * a.scale, dqt[db][4 * r4 + 1] * a.scale),
-                                    E::pack2(dqt[db][4 * r4 + 2] * a.scale, dqt[db][4 * r4 + 3] * a.scale)};
+        *(u32x2*)(qp + dim) =
+            u32x2{E::pack2(dqt[db % kDqt][4 * r4 + 0] * a.scale, dqt[db % kDqt][4 * r4 + 1] * a.scale),
+                  E::pack2(dqt[db % kDqt][4 * r4 + 2] * a.scale, dqt[db % kDqt][4 * r4 + 3] * a.scale)};
       }
     }
   }
+  };
+  if (role == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
 }
 
 }  // namespace bwd

@@ -184,3 +184,10 @@ def test_bwd_parity_workload_full_size(name):
     want = (do.double() * o.double()).sum(-1).numpy()
     err = float(np.max(np.abs(delta.double().numpy() - want)))
     assert err <= 1e-5 * max(1.0, float(np.max(np.abs(want)))), (name, "D", err)
+
+
+@pytest.mark.parametrize("causal,dtype", [(False, torch.bfloat16), (True, torch.float16)], ids=["bf16", "fp16-causal"])
+def test_bwd_parity_long_d128(causal, dtype):
+    """Head dim 128 on a long sequence with a ragged last tile (8195 rows =
+    64 * 128 + 3): 65 key and query workgroups per head."""
+    _parity(1, 1, 8195, 128, dtype, causal, seed=4)

@@ -161,3 +161,62 @@ def test_bwd_masked_reductions_match_plain_entry():
         b = fa.backward(qc, kc, vc, o, gc, lse, scale=0.125, **kw)
         for x, y in zip(a, b):
             assert torch.equal(x, y), kw
+
+
+@pytest.mark.parametrize("mask_name", ["window4096", "documents8"])
+def test_bwd_mask_workload_full_size(mask_name):
+    """The long-context causal workload (1 x 32 x 16384 x 128 fp16) under the two
+    masks the gradient benchmark times, at full size and in its launch
+    configuration: a causal window of 4096 keys (the last head against the
+    masked gradient oracle, whole), and 8 contiguous documents of 2048 rows
+    (each document is an independent causal sequence: the first and the last
+    document of the first and the last head against the causal gradient
+    oracle); every output finite."""
+    from exact_attention_11_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS["b1h32_n16384_d128_causal"]
+    dtype = w.torch_dtype
+    q, k, v = workload_inputs(w, seed=0)
+    do = _dout(q.shape, dtype, 0)
+    if mask_name == "window4096":
+        kw = dict(window=(4096, -1))
+    else:
+        seg = np.repeat(np.arange(8, dtype=np.int32), w.N // 8)[None].repeat(w.B, 0)
+        kw = dict(segment_ids=torch.from_numpy(np.ascontiguousarray(seg)).cuda())
+    _log(f"workload b1h32_n16384_d128_causal under {mask_name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}")
+    qc, kc, vc, gc = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.forward(qc, kc, vc, causal=w.causal, scale=w.scale, **kw)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = fa.backward(qc, kc, vc, o, gc, lse, causal=w.causal, scale=w.scale, delta=delta, **kw)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all(), mask_name
+    s32 = float(np.float32(w.scale))
+    checks = []
+    if mask_name == "window4096":
+        b, h = w.B - 1, w.H - 1
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv, _ = oracle.attention_bwd_masked_f64(q[sl].double().numpy(), k[sl].double().numpy(),
+                                                        v[sl].double().numpy(), do[sl].double().numpy(), s32,
+                                                        window_left=4096, window_right=-1, causal=True)
+        checks.append((f"(b={b},h={h})", sl, rq, rk, rv))
+    else:
+        n = w.N // 8
+        for h in (0, w.H - 1):
+            for doc in (0, 7):
+                sl = (slice(0, 1), slice(h, h + 1), slice(n * doc, n * (doc + 1)))
+                rq, rk, rv, _ = oracle.attention_bwd_f64(q[sl].double().numpy(), k[sl].double().numpy(),
+                                                         v[sl].double().numpy(), do[sl].double().numpy(), True, s32)
+                checks.append((f"(h={h}, document {doc})", sl, rq, rk, rv))
+    for what, sl, rq, rk, rv in checks:
+        for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            g = got[sl].double().numpy()
+            top = float(np.max(np.abs(ref)))
+            err = float(np.max(np.abs(g - ref)))
+            tol = REL * UNIT[dtype] * top + 1e-6
+            _log(f"  {mask_name} {what} {name}: max|d|={err:.3e} max|ref|={top:.3e} rel={err / top:.2e} tol={tol:.2e}")
+            assert err <= tol, (mask_name, what, name, err, tol)
+    want = (gc.double() * o.double()).sum(-1)
+    err = float((delta.double() - want).abs().max())
+    assert err <= 1e-5 * max(1.0, float(want.abs().max())), (mask_name, "D", err)

@@ -167,3 +167,46 @@ def test_mask_argument_errors():
         fa.forward(q, q, q, prefix=-1)
     with pytest.raises(ValueError):
         fa.forward(q, q, q, segment_ids=torch.zeros(1, 8, dtype=torch.int64, device="cuda"))
+
+
+@pytest.mark.parametrize("mask_name", ["window4096", "documents8"])
+def test_mask_workload_full_size(mask_name):
+    """The long-context causal workload (1 x 32 x 16384 x 128 fp16, inputs as
+    the benchmark draws them) at full size under the two masks the benchmark
+    times: a causal window of 4096 keys (the last head, whole, against the
+    masked oracle) and 8 contiguous documents of 2048 rows (each document an
+    independent causal sequence: the first and the last document of the first
+    and the last head against the plain causal oracle); every output finite."""
+    from exact_attention_11_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS["b1h32_n16384_d128_causal"]
+    q, k, v = workload_inputs(w, seed=0)
+    if mask_name == "window4096":
+        kw = dict(window=(4096, -1))
+    else:
+        seg = np.repeat(np.arange(8, dtype=np.int32), w.N // 8)[None].repeat(w.B, 0)
+        kw = dict(segment_ids=torch.from_numpy(np.ascontiguousarray(seg)).cuda())
+    _log(f"workload b1h32_n16384_d128_causal under {mask_name}")
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, scale=w.scale, **kw)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    s32 = float(np.float32(w.scale))
+    if mask_name == "window4096":
+        sl = (slice(0, 1), slice(w.H - 1, w.H))
+        refs = [(sl,) + tuple(oracle.attention_masked_f64(q[sl].double().numpy(), k[sl].double().numpy(),
+                                                          v[sl].double().numpy(), s32, window_left=4096,
+                                                          window_right=-1, causal=True))]
+    else:
+        n = w.N // 8
+        refs = []
+        for h in (0, w.H - 1):
+            for doc in (0, 7):
+                sl = (0, h, slice(n * doc, n * (doc + 1)))
+                refs.append((sl,) + tuple(oracle.attention_f64(q[sl].double().numpy(), k[sl].double().numpy(),
+                                                               v[sl].double().numpy(), True, s32)))
+    for sl, o_ref, l_ref in refs:
+        do = float(np.max(np.abs(o[sl] - o_ref)))
+        dl = float(np.max(np.abs(lse[sl] - l_ref)))
+        _log(f"  {mask_name} {sl}: max|dO|={do:.3e} max|dL|={dl:.3e}")
+        assert do <= TOL_O[torch.float16] and dl <= TOL_L, (mask_name, sl, do, dl)
